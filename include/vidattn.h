@@ -1,0 +1,156 @@
+/*
+ * vidattn.h — C ABI of libvidattn: 3D rotary position embedding and full
+ * (non-causal) spatiotemporal self-attention for video diffusion
+ * transformer blocks, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. The vidax paper summary (paperlayer.ai/abs/2609.18077v1,
+ * section 2 "System Architecture & Design", heading "3D RoPE, 3D VAEs, and
+ * flash attention") names 3D rotary embeddings and a flash-attention kernel
+ * that never materialises the quadratic query-key matrix; section 1
+ * ("Motivation and gap") describes the input as tens of thousands of tokens
+ * cut from a video latent as 3D patches. The pages do not write the rotary
+ * rule out; this library fixes it as follows (the plainest reading):
+ *
+ *   token order   n = (f*H + y)*W + x for a grid of F frames, H rows, W
+ *                 columns (frame-major);
+ *   chunks        the head dimension d splits into contiguous chunks
+ *                 [0, d_t) | [d_t, d_t+d_h) | [d_t+d_h, d) driven by the
+ *                 frame index f, row index y and column index x;
+ *   pairs         inside a chunk of width d_a starting at c0, the adjacent
+ *                 pair (c0+2j, c0+2j+1), j < d_a/2, is rotated by the angle
+ *                 phi = pos_a * theta^(-2j/d_a):
+ *                   x'[c0+2j]   = x[c0+2j]*cos(phi) - x[c0+2j+1]*sin(phi)
+ *                   x'[c0+2j+1] = x[c0+2j]*sin(phi) + x[c0+2j+1]*cos(phi)
+ *                 with 0-based integer positions (position (0,0,0) is the
+ *                 identity).
+ *
+ * Attention is O[i] = sum_j softmax_j(scale * <q'_i, k'_j>) v_j over all N
+ * tokens of one (batch, head) slice, with q', k' the rotated queries and
+ * keys (v is not rotated).
+ *
+ * Layout. Q, K, V and O are dense, contiguous [B][heads][N][d] row-major
+ * arrays (token rows of d elements, head-major: the layout an attention
+ * kernel sees after a sequence-to-head all-to-all).
+ *
+ * Memory. Every pointer argument is a device pointer owned by the caller
+ * (for example from PyTorch). The library allocates no device memory and
+ * keeps no state besides its code objects; q, k and v are only read.
+ *
+ * Streams. Work is enqueued on `hip_stream` (a hipStream_t; NULL means the
+ * null stream) and the call returns without synchronising. Faults of a
+ * kernel surface on the caller's next synchronisation.
+ *
+ * Errors. Every entry point returns a vidattn_status. Arguments are
+ * validated before any HIP call, so a malformed call returns INVALID_ARG or
+ * UNSUPPORTED without touching the device (and works without a GPU); no
+ * entry point aborts, throws or prints. vidattn_last_error() gives a
+ * human-readable detail of the last non-OK status on the calling thread.
+ *
+ * Numerics (bf16 path). Rotation and softmax run in fp32. The rotated keys
+ * and the rotated queries pre-multiplied by scale*log2(e) are rounded once,
+ * to nearest-even, to fp16 and multiplied on fp16 matrix cores with fp32
+ * accumulation (fp16 keeps 3 more mantissa bits than bf16; bf16 operands
+ * here lose the peaky-key accuracy bound). Softmax probabilities are
+ * rounded to nearest-even bf16 and multiplied with the bf16 V on bf16
+ * matrix cores with fp32 accumulation; O is rounded once to bf16.
+ * Finite results need |rotated k| < 65504 and |rotated q*scale*log2 e| <
+ * 65504. (fp32 path) Everything in fp32, fp32 matrix cores.
+ * Results are bitwise reproducible run to run for the same inputs.
+ */
+#ifndef VIDATTN_H
+#define VIDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VIDATTN_ABI_VERSION 1
+
+typedef enum {
+  VIDATTN_OK = 0,
+  VIDATTN_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, inconsistent grid or split */
+  VIDATTN_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (e.g. head dim 96) */
+  VIDATTN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than vidattn_fwd_workspace_size */
+  VIDATTN_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} vidattn_status;
+
+typedef enum {
+  VIDATTN_BF16 = 0,
+  VIDATTN_F16 = 1,
+  VIDATTN_F32 = 2
+} vidattn_dtype;
+
+/* Token grid and rotary parameters.
+ *   F, H, W       grid extents (frames, rows, columns), each >= 1; the
+ *                 sequence length N must equal F*H*W.
+ *   d_t, d_h, d_w widths of the frame, row and column chunks of the head
+ *                 dimension: each even and >= 0, d_t + d_h + d_w == d.
+ *   theta         frequency base (> 0 and finite), e.g. 10000.0. */
+typedef struct {
+  int64_t F, H, W;
+  int32_t d_t, d_h, d_w;
+  double theta;
+} vidattn_rope3d_desc;
+
+/* Standalone 3D rotary embedding (the rule above), for queries or keys.
+ *   in       [B][heads][N][d] with N = F*H*W, dtype in_dt (BF16 or F32).
+ *   out      same shape, dtype out_dt (BF16, F16 or F32); out == in is
+ *            allowed when both dtypes have the same size, any other overlap
+ *            is not.
+ *   prescale multiplies every rotated element (1.0f = none); finite.
+ *   d        even, a multiple of 8, at most 256.
+ * The rotation is computed in fp32 from fp64-evaluated cos/sin rounded to
+ * fp32, then multiplied by prescale and rounded to nearest-even to out_dt.
+ * Pointers must be 16-byte aligned. */
+vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt,
+                              int64_t B, int64_t heads, int64_t d, const vidattn_rope3d_desc* rope,
+                              float prescale, void* hip_stream);
+
+/* Attention forward: o = softmax(scale * rot(q) rot(k)^T) v per (b, head).
+ *   q, k, v, o    [B][heads][N][d], dtype dt (BF16 or F32); o has dtype dt.
+ *   d             64 or 128.
+ *   softmax_scale finite, > 0 (typically 1/sqrt(d)).
+ *   rope          NULL: q and k are used as given (already rotated or no
+ *                 rotary embedding). Otherwise the rotation is applied to q
+ *                 at tile load and to k by a pre-pass into the workspace;
+ *                 rope->F*H*W must equal N.
+ *   workspace     device buffer of at least
+ *                 vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != NULL)
+ *                 bytes, 256-byte aligned; it may be NULL only when that size
+ *                 is 0. Its contents on entry are irrelevant and are
+ *                 overwritten.
+ * All N keys are attended by every query (no mask, no causal order).
+ * Pointers must be 16-byte aligned; o must not overlap q, k, v or the
+ * workspace. */
+vidattn_status vidattn_fwd(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt,
+                           int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                           const vidattn_rope3d_desc* rope, void* workspace, size_t workspace_bytes,
+                           void* hip_stream);
+
+/* Workspace bytes vidattn_fwd needs for these sizes (0 if none). Returns 0
+ * also for arguments vidattn_fwd would reject; a positive size never
+ * depends on the data. BF16: the rotated fp16 keys and a transposed copy of
+ * V, tiled; 4*B*heads*ceil(N/64)*64*d bytes. F32: the rotated fp32 keys
+ * when use_rope, 4*B*heads*N*d bytes; else 0. */
+size_t vidattn_fwd_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                  int use_rope);
+
+/* Static text for a status code (never NULL). */
+const char* vidattn_status_string(vidattn_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if
+ * none). The pointer stays valid until the next vidattn_* call on that
+ * thread. */
+const char* vidattn_last_error(void);
+
+/* VIDATTN_ABI_VERSION of the loaded library. */
+int vidattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIDATTN_H */

@@ -1,0 +1,127 @@
+"""The C ABI on the CPU: the library loads, exports every function the
+header declares, and rejects malformed calls with the documented status
+before touching any device. Only calls that fail validation are made here
+(the pointers are fake and never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import video_diffusion_transformer_rope3d_amd as va
+from video_diffusion_transformer_rope3d_amd import Rope3dDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vidattn.h")
+
+P = 0x10000  # fake, 16-byte aligned device addresses (never dereferenced)
+Q, K, V, O, WS = P, 2 * P, 3 * P, 4 * P, 5 * P
+GOOD = Rope3dDesc.make((21, 45, 80), (44, 42, 42), 1e4)
+N5 = 75600
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(vidattn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_exactly_the_exported_set():
+    assert header_functions() == sorted(va.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_header_symbol():
+    lib = ctypes.CDLL(va.lib_path())
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strings():
+    assert va.vidattn_abi_version() == 1
+    for s, txt in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "workspace too small"),
+                   (4, "HIP error")]:
+        assert va.vidattn_status_string(s) == txt
+    assert va.vidattn_status_string(99) == "unknown status"
+
+
+def test_workspace_size():
+    ws = va.vidattn_fwd_workspace_size
+    assert ws(va.BF16, 2, 40, N5, 128, 1) == 4 * 80 * 75648 * 128
+    assert ws(va.BF16, 2, 40, N5, 128, 0) == 4 * 80 * 75648 * 128
+    assert ws(va.BF16, 1, 1, 1, 64, 1) == 4 * 64 * 64
+    assert ws(va.F32, 1, 4, 256, 64, 1) == 4 * 4 * 256 * 64
+    assert ws(va.F32, 1, 4, 256, 64, 0) == 0
+    assert ws(va.BF16, 1, 4, 256, 96, 1) == 0
+    assert ws(va.BF16, 0, 4, 256, 64, 1) == 0
+
+
+def fwd(q=Q, k=K, v=V, o=O, dt=va.BF16, B=2, H=40, N=N5, d=128, scale=0.088, rope=GOOD, ws=WS, wsb=None):
+    if wsb is None:
+        wsb = va.vidattn_fwd_workspace_size(dt, max(B, 1), max(H, 1), max(N, 1), d, rope is not None) or 0
+    return va.vidattn_fwd(q, k, v, o, dt, B, H, N, d, scale, rope, ws, wsb), va.vidattn_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "non-null"),
+    (dict(o=None), 1, "non-null"),
+    (dict(k=K + 8), 1, "aligned"),
+    (dict(dt=va.F16), 2, "dtype"),
+    (dict(dt=7), 1, "dtype"),
+    (dict(B=0), 1, ">= 1"),
+    (dict(N=0), 1, ">= 1"),
+    (dict(d=96), 2, "head dim"),
+    (dict(d=63), 1, "even"),
+    (dict(scale=0.0), 1, "softmax_scale"),
+    (dict(scale=float("nan")), 1, "softmax_scale"),
+    (dict(scale=float("inf")), 1, "softmax_scale"),
+    (dict(N=N5 - 1), 1, "does not equal N"),
+    (dict(rope=Rope3dDesc.make((21, 45, 80), (44, 42, 40))), 1, "sum"),
+    (dict(rope=Rope3dDesc.make((21, 45, 80), (43, 43, 42))), 1, "even"),
+    (dict(rope=Rope3dDesc.make((21, 45, 80), (44, 42, 42), 0.0)), 1, "theta"),
+    (dict(rope=Rope3dDesc.make((21, 45, 80), (44, 42, 42), float("nan"))), 1, "theta"),
+    (dict(rope=Rope3dDesc.make((0, 45, 80), (44, 42, 42))), 1, "extents"),
+    (dict(ws=None), 3, "workspace"),
+    (dict(wsb=1000), 3, "workspace"),
+    (dict(ws=WS + 16), 1, "256-byte"),
+    (dict(o=Q), 1, "overlap"),
+    (dict(o=WS), 1, "overlap"),
+    (dict(B=1 << 40), 1, "overflow"),
+])
+def test_fwd_rejects(kw, status, needle):
+    s, msg = fwd(**kw)
+    assert s == status, (s, msg)
+    assert needle in msg
+
+
+def test_fwd_f32_without_rope_needs_no_workspace_but_checks_overlap():
+    # a valid call shape would launch; make it fail on overlap instead
+    s, msg = fwd(dt=va.F32, rope=None, ws=None, wsb=0, o=K)
+    assert s == 1 and "overlap" in msg
+
+
+def rope_call(inp=Q, in_dt=va.BF16, out=O, out_dt=va.F16, B=2, H=40, d=128, rope=GOOD, prescale=1.0):
+    return va.vidattn_rope3d(inp, in_dt, out, out_dt, B, H, d, rope, prescale), va.vidattn_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(inp=None), 1, "non-null"),
+    (dict(rope=None), 1, "non-null"),
+    (dict(out=O + 4), 1, "aligned"),
+    (dict(in_dt=va.F16), 2, "dtype"),
+    (dict(out_dt=9), 1, "dtype"),
+    (dict(d=127), 1, "even"),
+    (dict(d=130), 2, "multiples of 8"),
+    (dict(d=264), 2, "multiples of 8"),
+    (dict(rope=Rope3dDesc.make((21, 45, 80), (44, 42, 44))), 1, "sum"),
+    (dict(prescale=float("inf")), 1, "prescale"),
+    (dict(out=Q + 16), 1, "overlap"),
+    (dict(out=Q, out_dt=va.F32), 1, "in-place"),
+])
+def test_rope_rejects(kw, status, needle):
+    s, msg = rope_call(**kw)
+    assert s == status, (s, msg)
+    assert needle in msg
+
+
+def test_last_error_is_per_call():
+    fwd(q=None)
+    assert va.vidattn_last_error() != ""

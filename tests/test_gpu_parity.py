@@ -1,0 +1,205 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle on
+the same seeded inputs, plus structural invariants. Needs an MI355X."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wlmod
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def va():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import video_diffusion_transformer_rope3d_amd as m
+    return m
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ rotation alone
+
+def _ulp(x, mant_bits):
+    ax = np.maximum(np.abs(x), 2.0 ** -14 if mant_bits == 10 else 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - mant_bits)
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("bf16", "f16"), ("bf16", "f32"), ("f32", "f32"),
+                                          ("f32", "bf16")])
+@pytest.mark.parametrize("shape", [((4, 8, 8), 64, (16, 24, 24)), ((21, 30, 52), 128, (44, 42, 42)),
+                                   ((3, 5, 7), 128, (44, 42, 42))])
+def test_rope3d_standalone(va, in_dt, out_dt, shape):
+    grid, d, split = shape
+    wl = wlmod.custom(2, 3, grid, d, split, dtype=in_dt, seed_id=300, std=(1.0, 1.0, 1.0))
+    _log(f"rope3d {in_dt}->{out_dt} grid={grid} d={d}")
+    x_h = wlmod.full(wl, "q")
+    x = parity.to_torch(x_h)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out_dt]
+    prescale = 0.75
+    y = va.rope3d(x, grid, split, wl.theta, out_dtype=tdt, prescale=prescale)
+    torch.cuda.synchronize()
+    got = parity.from_torch(y) if out_dt != "f16" else y.double().cpu().numpy()
+    ref = oracle.rope3d(parity.decode(wl, x_h), grid, split, wl.theta) * prescale
+    err = np.abs(got - ref)
+    mag = 1.0 + np.abs(ref)
+    if out_dt == "f32":
+        tol = 2e-6 * mag
+    else:
+        tol = 0.5 * _ulp(ref, 7 if out_dt == "bf16" else 10) + 2e-6 * mag
+    assert np.all(err <= tol), float(np.max(err - tol))
+
+
+def test_rope3d_in_place_matches_out_of_place(va):
+    wl = wlmod.custom(1, 2, (5, 6, 7), 128, (44, 42, 42), seed_id=301)
+    x = parity.to_torch(wlmod.full(wl, "k"))
+    a = va.rope3d(x, wl.grid, wl.split, 1e4)
+    va.rope3d(x, wl.grid, wl.split, 1e4, out=x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), x.view(torch.int16))
+
+
+# ------------------------------------------------------------------ attention, small shapes (every row)
+
+SMALL = [
+    # grid, d, split, dtype, B, heads
+    ((1, 1, 1), 128, (44, 42, 42), "bf16", 1, 1),     # N = 1
+    ((1, 1, 7), 64, (16, 24, 24), "bf16", 1, 2),      # N = 7 < one tile
+    ((2, 4, 8), 128, (44, 42, 42), "bf16", 1, 1),     # N = 64, one full key tile
+    ((3, 5, 7), 128, (44, 42, 42), "bf16", 2, 2),     # N = 105, ragged
+    ((2, 9, 11), 64, (16, 24, 24), "bf16", 1, 3),     # N = 198, d = 64
+    ((3, 11, 17), 128, (44, 42, 42), "bf16", 1, 2),   # N = 561: several tiles + tail
+    ((5, 13, 17), 128, (44, 42, 42), "bf16", 1, 1),   # N = 1105
+    ((4, 8, 8), 64, (16, 24, 24), "f32", 1, 4),       # the fp32 workload shape
+    ((3, 5, 7), 128, (44, 42, 42), "f32", 2, 1),      # fp32 d=128, ragged
+    ((1, 1, 1), 64, (16, 24, 24), "f32", 1, 1),       # fp32 N = 1
+    ((3, 7, 9), 64, (0, 32, 32), "f32", 1, 2),        # empty frame chunk
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[3]}-{c[0][0]}x{c[0][1]}x{c[0][2]}-d{c[1]}")
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
+def test_attention_small(va, case, rope):
+    grid, d, split, dt, B, H = case
+    wl = wlmod.custom(B, H, grid, d, split, dtype=dt, seed_id=400 + d + len(grid),
+                      std=(1.0, 1.0, 1.0) if dt == "f32" else (0.5, 0.5, 0.5))
+    _log(f"attention {wl.name} rope={rope}")
+    host = parity.host_inputs(wl)
+    o = parity.run_gpu(wl, host, rope=rope)
+    torch.cuda.synchronize()
+    st = parity.compare(wl, host, o, rope=rope)
+    _log(f"  {st}")
+    assert parity.within(wl, st), st
+
+
+# ------------------------------------------------------------------ the five workloads (sampled rows)
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_workload_parity(va, wid):
+    wl = wlmod.WORKLOADS[wid]
+    _log(f"workload {wl.name}: generating inputs")
+    host = parity.host_inputs(wl)
+    _log("  running HIP path")
+    o = parity.run_gpu(wl, host)
+    torch.cuda.synchronize()
+    _log("  oracle on sampled rows")
+    st = parity.compare(wl, host, o)
+    _log(f"  {st}")
+    assert parity.within(wl, st), st
+    del o
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ invariants (no oracle)
+
+def _rand(shape, dt, seed, std=0.5):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * std
+    return x.to(dt).cuda()
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_zero_query_gives_mean_of_v(va, dt):
+    grid, split = (3, 6, 9), (44, 42, 42)
+    shape = (1, 2, 162, 128)
+    q = torch.zeros(shape, dtype=dt, device="cuda")
+    k, v = _rand(shape, dt, 1), _rand(shape, dt, 2)
+    o = va.attention(q, k, v, grid=grid, split=split)
+    ref = v.double().mean(dim=2, keepdim=True).expand_as(o)
+    tol = 1e-5 if dt == torch.float32 else 4e-3
+    assert (o.double() - ref).abs().max().item() <= tol
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_unit_values_give_one(va, dt):
+    shape = (2, 2, 300, 128)
+    q, k = _rand(shape, dt, 3, 1.0), _rand(shape, dt, 4, 1.0)
+    v = torch.ones(shape, dtype=dt, device="cuda")
+    o = va.attention(q, k, v, grid=(3, 10, 10), split=(44, 42, 42))
+    tol = 1e-6 if dt == torch.float32 else 4e-3
+    assert (o.double() - 1.0).abs().max().item() <= tol
+
+
+def test_single_token_gives_v(va):
+    shape = (2, 3, 1, 128)
+    q, k, v = (_rand(shape, torch.bfloat16, s) for s in (5, 6, 7))
+    o = va.attention(q, k, v, grid=(1, 1, 1), split=(44, 42, 42))
+    assert torch.equal(o.view(torch.int16), v.view(torch.int16))
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_bitwise_deterministic_and_overwrites_poison(va, dt):
+    shape = (2, 4, 1105, 128)
+    q, k, v = (_rand(shape, dt, s) for s in (8, 9, 10))
+    o1 = torch.full(shape, float("nan"), dtype=dt, device="cuda")
+    o2 = torch.full(shape, float("nan"), dtype=dt, device="cuda")
+    va.attention(q, k, v, grid=(5, 13, 17), split=(44, 42, 42), out=o1)
+    va.attention(q, k, v, grid=(5, 13, 17), split=(44, 42, 42), out=o2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all()
+    assert torch.equal(o1.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                       o2.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+
+
+def test_guard_regions_untouched(va):
+    """Outputs and workspace are written only inside their extents."""
+    shape = (1, 2, 561, 128)
+    n = math.prod(shape)
+    guard = 4096
+    q, k, v = (_rand(shape, torch.bfloat16, s) for s in (11, 12, 13))
+    obuf = torch.full((n + 2 * guard,), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = obuf[guard:guard + n].view(shape)
+    wsn = va.vidattn_fwd_workspace_size(va.BF16, 1, 2, 561, 128, True)
+    wbuf = torch.full((wsn + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = wbuf[guard:guard + wsn]
+    va.attention(q, k, v, grid=(3, 11, 17), split=(44, 42, 42), out=o, workspace=ws)
+    torch.cuda.synchronize()
+    assert (obuf[:guard] == 7.0).all() and (obuf[guard + n:] == 7.0).all()
+    assert (wbuf[:guard] == 0x5A).all() and (wbuf[guard + wsn:] == 0x5A).all()
+
+
+def test_no_rope_matches_prerotated(va):
+    """rope=NULL with pre-rotated fp32 inputs equals the fused rotation."""
+    wl = wlmod.custom(1, 2, (3, 5, 7), 128, (44, 42, 42), dtype="f32", seed_id=500, std=(1, 1, 1))
+    host = parity.host_inputs(wl)
+    q, k, v = (parity.to_torch(host[n]) for n in ("q", "k", "v"))
+    qr = va.rope3d(q, wl.grid, wl.split, wl.theta)
+    kr = va.rope3d(k, wl.grid, wl.split, wl.theta)
+    a = va.attention(q, k, v, grid=wl.grid, split=wl.split, theta=wl.theta)
+    b = va.attention(qr, kr, v)
+    torch.cuda.synchronize()
+    assert (a - b).abs().max().item() <= 2e-6
+
+
+def test_error_status_raises(va):
+    q = torch.zeros((1, 1, 10, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(va.VidattnError) as e:
+        va.attention(q, q.clone(), q.clone())
+    assert e.value.status == 2

@@ -1,0 +1,200 @@
+"""Python binding of libvidattn (3D-RoPE full attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libvidattn.so``; PyTorch supplies device memory and streams.
+The low-level functions carry the C names (``vidattn_fwd`` ...) and take
+raw device pointers; ``attention`` and ``rope3d`` accept torch tensors.
+Importing this package loads the library and raises if it is missing;
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "BF16", "F16", "F32", "VidattnError", "Rope3dDesc", "lib_path", "load",
+    "vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_workspace_size", "vidattn_status_string",
+    "vidattn_last_error", "vidattn_abi_version", "attention", "rope3d", "workspace_for",
+    "EXPORTED_SYMBOLS",
+]
+
+BF16, F16, F32 = 0, 1, 2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+ABI_VERSION = 1
+
+EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_workspace_size", "vidattn_status_string",
+                    "vidattn_last_error", "vidattn_abi_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.environ.get("VIDATTN_LIB", os.path.join(_HERE, "libvidattn.so"))
+
+
+class VidattnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"vidattn status {status} ({_status_text(status)}): {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class Rope3dDesc(ctypes.Structure):
+    _fields_ = [("F", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
+                ("d_t", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_w", ctypes.c_int32),
+                ("theta", ctypes.c_double)]
+
+    @classmethod
+    def make(cls, grid, split, theta=10000.0) -> "Rope3dDesc":
+        F, H, W = (int(g) for g in grid)
+        d_t, d_h, d_w = (int(s) for s in split)
+        return cls(F, H, W, d_t, d_h, d_w, float(theta))
+
+
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libvidattn.so once; raises ImportError if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"libvidattn.so not found at {path}; build it with "
+                          "`python -m video_diffusion_transformer_rope3d_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.vidattn_rope3d.restype = ctypes.c_int
+    lib.vidattn_rope3d.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64,
+                                   ctypes.POINTER(Rope3dDesc), ctypes.c_float, vp]
+    lib.vidattn_fwd.restype = ctypes.c_int
+    lib.vidattn_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
+                                ctypes.POINTER(Rope3dDesc), vp, sz, vp]
+    lib.vidattn_fwd_workspace_size.restype = sz
+    lib.vidattn_fwd_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
+    lib.vidattn_status_string.restype = ctypes.c_char_p
+    lib.vidattn_status_string.argtypes = [ctypes.c_int]
+    lib.vidattn_last_error.restype = ctypes.c_char_p
+    lib.vidattn_last_error.argtypes = []
+    lib.vidattn_abi_version.restype = ctypes.c_int
+    lib.vidattn_abi_version.argtypes = []
+    if lib.vidattn_abi_version() != ABI_VERSION:
+        raise ImportError(f"libvidattn ABI {lib.vidattn_abi_version()} != binding ABI {ABI_VERSION}")
+    _LIB = lib
+    return lib
+
+
+def _status_text(s: int) -> str:
+    return load().vidattn_status_string(s).decode()
+
+
+# ------------------------------------------------------------------ C names, raw pointers
+
+def vidattn_rope3d(inp, in_dt, out, out_dt, B, heads, d, rope, prescale=1.0, stream=None) -> int:
+    return load().vidattn_rope3d(inp, in_dt, out, out_dt, B, heads, d,
+                                 ctypes.byref(rope) if rope is not None else None, prescale, stream)
+
+
+def vidattn_fwd(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, workspace, workspace_bytes,
+                stream=None) -> int:
+    return load().vidattn_fwd(q, k, v, o, dt, B, heads, N, d, softmax_scale,
+                              ctypes.byref(rope) if rope is not None else None, workspace, workspace_bytes,
+                              stream)
+
+
+def vidattn_fwd_workspace_size(dt, B, heads, N, d, use_rope) -> int:
+    return load().vidattn_fwd_workspace_size(dt, B, heads, N, d, int(bool(use_rope)))
+
+
+def vidattn_status_string(s: int) -> str:
+    return _status_text(s)
+
+
+def vidattn_last_error() -> str:
+    return load().vidattn_last_error().decode()
+
+
+def vidattn_abi_version() -> int:
+    return load().vidattn_abi_version()
+
+
+def _raise(status: int):
+    if status != OK:
+        raise VidattnError(status, vidattn_last_error())
+
+
+# ------------------------------------------------------------------ torch conveniences
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    m = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def workspace_for(q, use_rope: bool):
+    """A torch byte buffer of the size vidattn_fwd needs for q's shape (None if 0)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    n = vidattn_fwd_workspace_size(_dt(q), B, H, N, d, use_rope)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def attention(q, k, v, *, scale=None, grid=None, split=None, theta=10000.0, out=None, workspace=None,
+              stream=None):
+    """O = softmax(scale * rot(q) rot(k)^T) v for [B, heads, N, d] tensors.
+    With grid/split given, q and k are rotated by 3D RoPE inside the call;
+    otherwise they are used as given."""
+    B, H, N, d = q.shape
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [B, heads, N, d]")
+    if out is None:
+        out = _torch().empty_like(q)
+    rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
+    if workspace is None:
+        workspace = workspace_for(q, rope is not None)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _raise(vidattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(q), B, H, N, d, s, rope,
+                       ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def rope3d(x, grid, split, theta=10000.0, *, out=None, out_dtype=None, prescale=1.0, stream=None):
+    """3D rotary embedding of a [B, heads, N, d] tensor (out may be x)."""
+    torch = _torch()
+    B, H, N, d = x.shape
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if N != int(grid[0]) * int(grid[1]) * int(grid[2]):
+        raise ValueError(f"x has {N} tokens, grid {tuple(grid)} has {int(grid[0]) * int(grid[1]) * int(grid[2])}")
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _raise(vidattn_rope3d(x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), B, H, d,
+                          Rope3dDesc.make(grid, split, theta), prescale, _stream(stream)))
+    return out
+
+
+load()

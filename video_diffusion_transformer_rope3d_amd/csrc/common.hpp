@@ -1,0 +1,90 @@
+// Shared device helpers of libvidattn: vector types, conversions and the
+// 3D rotary angle of one (token, pair).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vidattn {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxPairs = 128;  // head dim up to 256
+
+// Rotary parameters as kernel arguments. Pair p (elements 2p, 2p+1) is
+// driven by the frame index when p < pair_t, by the row index when
+// p < pair_th, else by the column index; it turns by pos * omega[p].
+// omega[p] = theta^(-2j/d_a) for pair j of its axis chunk of width d_a,
+// evaluated on the host in double precision.
+struct RopeParams {
+  int enabled;
+  int F, H, W;
+  int pair_t, pair_th;
+  double omega[kMaxPairs];
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Unpack 8 bf16 (one 16-byte load) to fp32.
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Token index -> grid coordinates (frame-major order n = (f*H + y)*W + x),
+// then the coordinate driving pair p.
+__device__ __forceinline__ int rope_pos(const RopeParams& rp, int n, int p) {
+  const int hw = rp.H * rp.W;
+  const int f = n / hw;
+  const int r = n - f * hw;
+  const int y = r / rp.W;
+  const int x = r - y * rp.W;
+  return p < rp.pair_t ? f : (p < rp.pair_th ? y : x);
+}
+
+// cos/sin of the rotation angle of pair p of token n: the angle and its
+// cos/sin are evaluated in double precision and rounded once to fp32.
+__device__ __forceinline__ void rope_cos_sin(const RopeParams& rp, int n, int p, float& c, float& s) {
+  const double ang = (double)rope_pos(rp, n, p) * rp.omega[p];
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// Rotate one pair in fp32: (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
+__device__ __forceinline__ void rotate_pair(float& x0, float& x1, float c, float s) {
+  const float a = __builtin_fmaf(x0, c, -(x1 * s));
+  const float b = __builtin_fmaf(x0, s, x1 * c);
+  x0 = a;
+  x1 = b;
+}
+
+// Lanes l and l^32 exchange a value; returns the pair {x[l], x[l^32]} in
+// some order (enough for symmetric reductions such as max and sum).
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row index permutation of a 32-row MFMA operand block: swaps bits 2 and 3.
+// Loading key rho(i) into A-operand row i of the 32x32x16 score product
+// makes the 8 scores a lane holds per 16-key step belong to 8 consecutive
+// keys, so the P.V product can read V^T with one 16-byte load per lane.
+__device__ __host__ __forceinline__ int rho32(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+}  // namespace vidattn

@@ -1,0 +1,197 @@
+// 3D rotary embedding kernels (HBM-bound elementwise work):
+//   rope3d_kernel    standalone rotation of a [B][heads][N][d] tensor;
+//   prep_kv_kernel   the key/value pre-pass of the bf16 attention: rotated
+//                    keys rounded to fp16 and a transposed copy of V, both
+//                    written tile by tile in the order the matrix-core
+//                    operands are read, so the attention kernel copies
+//                    each tile linearly into LDS.
+#pragma once
+
+#include "common.hpp"
+
+namespace vidattn {
+
+// ---------------------------------------------------------------- loads/stores of 8 elements
+
+template <typename T>
+struct Elem8;
+
+template <>
+struct Elem8<uint16_t> {  // bf16 storage
+  static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) {
+    unpack_bf16x8(*reinterpret_cast<const u32x4*>(p), x);
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)x[i];
+    *reinterpret_cast<bf16x8*>(p) = v;
+  }
+};
+
+template <>
+struct Elem8<_Float16> {
+  static __device__ __forceinline__ void store(_Float16* p, const float (&x)[8]) {
+    half8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (_Float16)x[i];
+    *reinterpret_cast<half8*>(p) = v;
+  }
+};
+
+template <>
+struct Elem8<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&x)[8]) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+    const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&x)[8]) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = x[i];
+      b[i] = x[4 + i];
+    }
+    reinterpret_cast<f32x4*>(p)[0] = a;
+    reinterpret_cast<f32x4*>(p)[1] = b;
+  }
+};
+
+// ---------------------------------------------------------------- standalone rotation
+
+// One thread = one 8-element chunk (4 pairs) of one token; its 4 cos/sin
+// pairs are evaluated once and reused over `bh_per_block` (batch, head)
+// slices. grid = (ceil(N*d/8 / 256), ceil(B*heads / bh_per_block)).
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void rope3d_kernel(const TIn* in, TOut* out, int64_t nbh, int N, int d,
+                                                     float prescale, int bh_per_block, RopeParams rp) {
+  const int cpt = d >> 3;
+  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (item >= (int64_t)N * cpt) return;
+  const int n = (int)(item / cpt);
+  const int c = (int)(item - (int64_t)n * cpt);
+  float cs[4], sn[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rope_cos_sin(rp, n, 4 * c + j, cs[j], sn[j]);
+  const int64_t bh0 = (int64_t)blockIdx.y * bh_per_block;
+  const int64_t bh1 = bh0 + bh_per_block < nbh ? bh0 + bh_per_block : nbh;
+  for (int64_t bh = bh0; bh < bh1; ++bh) {
+    const int64_t off = (bh * N + n) * d + 8 * c;
+    float x[8];
+    Elem8<TIn>::load(in + off, x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      rotate_pair(x[2 * j], x[2 * j + 1], cs[j], sn[j]);
+      x[2 * j] *= prescale;
+      x[2 * j + 1] *= prescale;
+    }
+    Elem8<TOut>::store(out + off, x);
+  }
+}
+
+// ---------------------------------------------------------------- bf16 attention pre-pass
+
+// Workspace tile layout (per (b, head), per tile of KT = 64 keys; the
+// K part and the V part are TILE = 64*D*2 bytes each, K first):
+//   K part: 1 KB blocks, block (kb, s) for key block kb < 2 (32 keys) and
+//           head-dim step s < D/16; lane l = i + 32g of the block holds the
+//           16 bytes K'[32kb + rho32(i)][16s + 8g .. 16s + 8g + 7] (fp16,
+//           rotated). This is the A operand of v_mfma_f32_32x32x16_f16.
+//   V part: 1 KB blocks, block (db, m) for head-dim block db < D/32 and key
+//           step m < 4 (16 keys); lane l = i + 32g holds V[16m + 8g + j][32db + i],
+//           j < 8 (bf16): the A operand of the V^T.P^T product.
+// Keys past N are zero in both parts.
+template <int D>
+__global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                                      uint8_t* __restrict__ ws, int N, int nkt, int64_t nbh,
+                                                      int bh_per_block, RopeParams rp) {
+  constexpr int KT = 64;
+  constexpr int KSTEPS = D / 16;
+  constexpr int TILE = KT * D * 2;
+  constexpr int SLOTS = TILE / 16 / 256;  // 16-byte slots per thread per part
+  constexpr int VPAD = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t vs[KT * VPAD];
+
+  const int t = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int n0 = tile * KT;
+
+  int ksrc[SLOTS];  // source key of the slot (-1: past N)
+  int kchunk[SLOTS];
+  float cs[SLOTS][4], sn[SLOTS][4];
+#pragma unroll
+  for (int r = 0; r < SLOTS; ++r) {
+    const int slot = t + 256 * r;
+    const int blk = slot >> 6, lane = slot & 63;
+    const int i = lane & 31, g = lane >> 5;
+    const int kb = blk / KSTEPS, s = blk - kb * KSTEPS;
+    const int n = n0 + 32 * kb + rho32(i);
+    ksrc[r] = n < N ? n : -1;
+    kchunk[r] = 2 * s + g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cs[r][j] = 1.f;
+      sn[r][j] = 0.f;
+      if (rp.enabled && n < N) rope_cos_sin(rp, n, 4 * kchunk[r] + j, cs[r][j], sn[r][j]);
+    }
+  }
+
+  const int64_t bh0 = (int64_t)blockIdx.y * bh_per_block;
+  const int64_t bh1 = bh0 + bh_per_block < nbh ? bh0 + bh_per_block : nbh;
+  for (int64_t bh = bh0; bh < bh1; ++bh) {
+    const uint16_t* Kbh = K + bh * N * D;
+    const uint16_t* Vbh = V + bh * N * D;
+    uint8_t* wt = ws + (bh * nkt + tile) * (int64_t)(2 * TILE);
+
+    // keys: rotate, round to fp16, scatter into operand order
+#pragma unroll
+    for (int r = 0; r < SLOTS; ++r) {
+      half8 h;
+      if (ksrc[r] >= 0) {
+        float x[8];
+        Elem8<uint16_t>::load(Kbh + (int64_t)ksrc[r] * D + 8 * kchunk[r], x);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rotate_pair(x[2 * j], x[2 * j + 1], cs[r][j], sn[r][j]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = (_Float16)x[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = (_Float16)0.f;
+      }
+      *reinterpret_cast<half8*>(wt + (t + 256 * r) * 16) = h;
+    }
+
+    // values: stage the row-major tile in LDS, then gather 8 keys per slot
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < SLOTS; ++r) {
+      const int ch = t + 256 * r;
+      const int row = ch / (D / 8), col8 = ch - row * (D / 8);
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (n0 + row < N) w = *reinterpret_cast<const u32x4*>(Vbh + (int64_t)(n0 + row) * D + 8 * col8);
+      *reinterpret_cast<u32x4*>(vs + row * VPAD + 8 * col8) = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < SLOTS; ++r) {
+      const int slot = t + 256 * r;
+      const int blk = slot >> 6, lane = slot & 63;
+      const int i = lane & 31, g = lane >> 5;
+      const int db = blk >> 2, m = blk & 3;
+      const int col = 32 * db + i;
+      const int key0 = 16 * m + 8 * g;
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)vs[(key0 + 2 * j) * VPAD + col] | ((uint32_t)vs[(key0 + 2 * j + 1) * VPAD + col] << 16);
+      *reinterpret_cast<u32x4*>(wt + TILE + slot * 16) = w;
+    }
+  }
+}
+
+}  // namespace vidattn

@@ -1,0 +1,302 @@
+// libvidattn: C ABI entry points (declared and documented in include/vidattn.h).
+// Host side: argument validation (before any HIP call), rotary parameter
+// setup, workspace sizing and kernel launches on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "vidattn.h"
+#include "attn_bf16.hpp"
+#include "attn_f32.hpp"
+#include "rope_kernels.hpp"
+
+using namespace vidattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vidattn_status fail(vidattn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+vidattn_status ok() {
+  g_last_error.clear();
+  return VIDATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_size(vidattn_dtype dt) {
+  switch (dt) {
+    case VIDATTN_BF16:
+    case VIDATTN_F16:
+      return 2;
+    case VIDATTN_F32:
+      return 4;
+  }
+  return 0;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+
+// Limits that keep every in-kernel index within 32/64-bit range and the
+// launch grid within the hardware's limits.
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxBH = int64_t(1) << 20;
+
+constexpr int kKT = 64;  // keys per tile of the bf16 attention kernel
+constexpr int kNW = 8;   // waves per workgroup of the bf16 attention kernel
+constexpr int kQB = 1;   // 32-query blocks per wave
+constexpr int kBR = kNW * kQB * 32;
+
+vidattn_status check_rope(const vidattn_rope3d_desc* r, int64_t d, int64_t N_expected, bool check_n) {
+  if (r->F < 1 || r->H < 1 || r->W < 1)
+    return fail(VIDATTN_ERR_INVALID_ARG, "rope grid extents must be >= 1 (got %lld x %lld x %lld)", (long long)r->F,
+                (long long)r->H, (long long)r->W);
+  int64_t hw, fhw;
+  if (!mul_ok(r->H, r->W, &hw) || !mul_ok(r->F, hw, &fhw) || fhw > kMaxN)
+    return fail(VIDATTN_ERR_INVALID_ARG, "rope grid F*H*W overflows or exceeds %lld tokens", (long long)kMaxN);
+  if (check_n && fhw != N_expected)
+    return fail(VIDATTN_ERR_INVALID_ARG, "rope grid F*H*W = %lld does not equal N = %lld", (long long)fhw,
+                (long long)N_expected);
+  if (r->d_t < 0 || r->d_h < 0 || r->d_w < 0 || (r->d_t & 1) || (r->d_h & 1) || (r->d_w & 1))
+    return fail(VIDATTN_ERR_INVALID_ARG, "rope split %d/%d/%d must be even, non-negative widths", r->d_t, r->d_h,
+                r->d_w);
+  if ((int64_t)r->d_t + r->d_h + r->d_w != d)
+    return fail(VIDATTN_ERR_INVALID_ARG, "rope split %d+%d+%d does not sum to head dim %lld", r->d_t, r->d_h,
+                r->d_w, (long long)d);
+  if (!std::isfinite(r->theta) || !(r->theta > 0.0))
+    return fail(VIDATTN_ERR_INVALID_ARG, "rope theta must be finite and > 0");
+  return VIDATTN_OK;
+}
+
+RopeParams make_rope(const vidattn_rope3d_desc* r) {
+  RopeParams p;
+  std::memset(&p, 0, sizeof p);
+  if (!r) return p;
+  p.enabled = 1;
+  p.F = (int)r->F;
+  p.H = (int)r->H;
+  p.W = (int)r->W;
+  p.pair_t = r->d_t / 2;
+  p.pair_th = (r->d_t + r->d_h) / 2;
+  int k = 0;
+  const int widths[3] = {r->d_t, r->d_h, r->d_w};
+  for (int a = 0; a < 3; ++a)
+    for (int j = 0; j < widths[a] / 2; ++j) p.omega[k++] = std::pow(r->theta, -2.0 * j / widths[a]);
+  return p;
+}
+
+vidattn_status hip_check(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(VIDATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return VIDATTN_OK;
+}
+
+int bh_group(int64_t items_blocks, int64_t nbh) {
+  // Reuse each block's cos/sin over several (b, head) slices while keeping
+  // at least ~4 blocks per CU in flight.
+  int g = 16;
+  while (g > 1 && items_blocks * ((nbh + g - 1) / g) < 1024) g >>= 1;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vidattn_abi_version(void) { return VIDATTN_ABI_VERSION; }
+
+const char* vidattn_status_string(vidattn_status s) {
+  switch (s) {
+    case VIDATTN_OK:
+      return "ok";
+    case VIDATTN_ERR_INVALID_ARG:
+      return "invalid argument";
+    case VIDATTN_ERR_UNSUPPORTED:
+      return "unsupported";
+    case VIDATTN_ERR_WORKSPACE:
+      return "workspace too small";
+    case VIDATTN_ERR_HIP:
+      return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* vidattn_last_error(void) { return g_last_error.c_str(); }
+
+size_t vidattn_fwd_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d, int use_rope) {
+  if (B < 1 || heads < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128)) return 0;
+  int64_t nbh;
+  if (!mul_ok(B, heads, &nbh) || nbh > kMaxBH) return 0;
+  if (dt == VIDATTN_BF16) {
+    const int64_t npad = (N + kKT - 1) / kKT * kKT;
+    return (size_t)(4 * nbh * npad * d);
+  }
+  if (dt == VIDATTN_F32) return use_rope ? (size_t)(4 * nbh * N * d) : 0;
+  return 0;
+}
+
+vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt, int64_t B,
+                              int64_t heads, int64_t d, const vidattn_rope3d_desc* rope, float prescale,
+                              void* hip_stream) {
+  if (!in || !out || !rope) return fail(VIDATTN_ERR_INVALID_ARG, "in, out and rope must be non-null");
+  if (!aligned16(in) || !aligned16(out)) return fail(VIDATTN_ERR_INVALID_ARG, "in and out must be 16-byte aligned");
+  if (in_dt != VIDATTN_BF16 && in_dt != VIDATTN_F32)
+    return fail(dtype_size(in_dt) ? VIDATTN_ERR_UNSUPPORTED : VIDATTN_ERR_INVALID_ARG,
+                "input dtype must be BF16 or F32");
+  if (!dtype_size(out_dt)) return fail(VIDATTN_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dt);
+  if (B < 1 || heads < 1 || d < 1) return fail(VIDATTN_ERR_INVALID_ARG, "B, heads and d must be >= 1");
+  int64_t nbh;
+  if (!mul_ok(B, heads, &nbh) || nbh > kMaxBH)
+    return fail(VIDATTN_ERR_INVALID_ARG, "B*heads overflows or exceeds %lld", (long long)kMaxBH);
+  if ((d & 1) != 0) return fail(VIDATTN_ERR_INVALID_ARG, "head dim %lld must be even", (long long)d);
+  if (d % 8 != 0 || d > 256)
+    return fail(VIDATTN_ERR_UNSUPPORTED, "head dim %lld: rotation supports multiples of 8 up to 256", (long long)d);
+  if (vidattn_status s = check_rope(rope, d, 0, false)) return s;
+  if (!std::isfinite(prescale)) return fail(VIDATTN_ERR_INVALID_ARG, "prescale must be finite");
+  const int64_t N = rope->F * rope->H * rope->W;
+  int64_t elems, bytes_in, bytes_out;
+  if (!mul_ok(nbh, N * d, &elems) || !mul_ok(elems, (int64_t)dtype_size(in_dt), &bytes_in) ||
+      !mul_ok(elems, (int64_t)dtype_size(out_dt), &bytes_out))
+    return fail(VIDATTN_ERR_INVALID_ARG, "tensor size overflows");
+  const char* ib = static_cast<const char*>(in);
+  const char* ob = static_cast<const char*>(out);
+  if (ib != ob && ib < ob + bytes_out && ob < ib + bytes_in)
+    return fail(VIDATTN_ERR_INVALID_ARG, "in and out overlap without being the same buffer");
+  if (ib == ob && dtype_size(in_dt) != dtype_size(out_dt))
+    return fail(VIDATTN_ERR_INVALID_ARG, "in-place rotation needs equal input and output element sizes");
+
+  const RopeParams rp = make_rope(rope);
+  const int64_t items = N * (d / 8);
+  const int64_t xblocks = (items + 255) / 256;
+  const int grp = bh_group(xblocks, nbh);
+  const dim3 grid((unsigned)xblocks, (unsigned)((nbh + grp - 1) / grp));
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+#define VIDATTN_ROPE_LAUNCH(TI, TO)                                                                                 \
+  hipLaunchKernelGGL((rope3d_kernel<TI, TO>), grid, dim3(256), 0, st, static_cast<const TI*>(in),                  \
+                     static_cast<TO*>(out), nbh, (int)N, (int)d, prescale, grp, rp)
+  if (in_dt == VIDATTN_BF16) {
+    if (out_dt == VIDATTN_BF16) VIDATTN_ROPE_LAUNCH(uint16_t, uint16_t);
+    else if (out_dt == VIDATTN_F16) VIDATTN_ROPE_LAUNCH(uint16_t, _Float16);
+    else VIDATTN_ROPE_LAUNCH(uint16_t, float);
+  } else {
+    if (out_dt == VIDATTN_BF16) VIDATTN_ROPE_LAUNCH(float, uint16_t);
+    else if (out_dt == VIDATTN_F16) VIDATTN_ROPE_LAUNCH(float, _Float16);
+    else VIDATTN_ROPE_LAUNCH(float, float);
+  }
+#undef VIDATTN_ROPE_LAUNCH
+  if (vidattn_status s = hip_check("rope3d launch")) return s;
+  return ok();
+}
+
+vidattn_status vidattn_fwd(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,
+                           int64_t heads, int64_t N, int64_t d, float softmax_scale, const vidattn_rope3d_desc* rope,
+                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!q || !k || !v || !o) return fail(VIDATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(VIDATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (dt != VIDATTN_BF16 && dt != VIDATTN_F32)
+    return fail(dt == VIDATTN_F16 ? VIDATTN_ERR_UNSUPPORTED : VIDATTN_ERR_INVALID_ARG,
+                "attention dtype must be BF16 or F32");
+  if (B < 1 || heads < 1 || N < 1 || d < 1) return fail(VIDATTN_ERR_INVALID_ARG, "B, heads, N and d must be >= 1");
+  int64_t nbh;
+  if (!mul_ok(B, heads, &nbh) || nbh > kMaxBH)
+    return fail(VIDATTN_ERR_INVALID_ARG, "B*heads overflows or exceeds %lld", (long long)kMaxBH);
+  if (N > kMaxN) return fail(VIDATTN_ERR_UNSUPPORTED, "N = %lld exceeds %lld", (long long)N, (long long)kMaxN);
+  if (d != 64 && d != 128) {
+    if (d & 1) return fail(VIDATTN_ERR_INVALID_ARG, "head dim %lld must be even", (long long)d);
+    return fail(VIDATTN_ERR_UNSUPPORTED, "head dim %lld: supported are 64 and 128", (long long)d);
+  }
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(VIDATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (rope)
+    if (vidattn_status s = check_rope(rope, d, N, true)) return s;
+  const size_t need = vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(VIDATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need,
+                  workspace ? workspace_bytes : (size_t)0, workspace ? "" : " (null)");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(VIDATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  {
+    const int64_t tensor_bytes = nbh * N * d * (int64_t)dtype_size(dt);
+    const char* ob = static_cast<const char*>(o);
+    const char* ins[3] = {static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v)};
+    for (const char* p : ins)
+      if (p < ob + tensor_bytes && ob < p + tensor_bytes)
+        return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps q, k or v");
+    if (need > 0) {
+      const char* w = static_cast<const char*>(workspace);
+      if (w < ob + tensor_bytes && ob < w + (int64_t)need) return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps the workspace");
+    }
+  }
+
+  const RopeParams rp = make_rope(rope);
+  const float log2e = 1.4426950408889634f;
+  const float qscale = softmax_scale * log2e;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+  if (dt == VIDATTN_BF16) {
+    const int nkt = (int)((N + kKT - 1) / kKT);
+    const int grp = bh_group(nkt, nbh);
+    const dim3 pgrid((unsigned)nkt, (unsigned)((nbh + grp - 1) / grp));
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const int ntq = (int)((N + kBR - 1) / kBR);
+    const int64_t total = nbh * ntq;
+    if (total > (int64_t)INT32_MAX / (kNW * 64))
+      return fail(VIDATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (d == 128) {
+      hipLaunchKernelGGL((prep_kv_kernel<128>), pgrid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, kNW, kQB>), dim3((unsigned)total), dim3(kNW * 64), 0, st,
+                         static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq,
+                         (int)total, qscale, rp);
+    } else {
+      hipLaunchKernelGGL((prep_kv_kernel<64>), pgrid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, kNW, kQB>), dim3((unsigned)total), dim3(kNW * 64), 0, st,
+                         static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq,
+                         (int)total, qscale, rp);
+    }
+    if (vidattn_status s = hip_check("bf16 attention launch")) return s;
+    return ok();
+  }
+
+  // fp32
+  const float* kk = static_cast<const float*>(k);
+  if (rope) {
+    const int64_t items = N * (d / 8);
+    const int64_t xblocks = (items + 255) / 256;
+    const int grp = bh_group(xblocks, nbh);
+    const dim3 grid((unsigned)xblocks, (unsigned)((nbh + grp - 1) / grp));
+    hipLaunchKernelGGL((rope3d_kernel<float, float>), grid, dim3(256), 0, st, kk, static_cast<float*>(workspace), nbh,
+                       (int)N, (int)d, 1.0f, grp, rp);
+    kk = static_cast<const float*>(workspace);
+  }
+  const int ntq = (int)((N + 127) / 128);
+  const int64_t total = nbh * ntq;
+  if (total > (int64_t)INT32_MAX / 256) return fail(VIDATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (d == 128)
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<128>), dim3((unsigned)total), dim3(256), 0, st,
+                       static_cast<const float*>(q), kk, static_cast<const float*>(v), static_cast<float*>(o), (int)N,
+                       ntq, qscale, rp);
+  else
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<64>), dim3((unsigned)total), dim3(256), 0, st,
+                       static_cast<const float*>(q), kk, static_cast<const float*>(v), static_cast<float*>(o), (int)N,
+                       ntq, qscale, rp);
+  if (vidattn_status s = hip_check("f32 attention launch")) return s;
+  return ok();
+}
+
+}  // extern "C"
