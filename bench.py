@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of 3D-RoPE full attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ID]
+
+A step is one fused ``vidattn_fwd`` call with the rotary descriptor (key
+pre-pass + attention kernel with the query rotation fused) over the whole
+workload, inputs resident in HBM. Default workload: 2 x 40 heads x 75600
+tokens (21x45x80 grid), head dim 128, bf16. FLOPs per call = 4*B*H*N^2*d.
+
+Prints ONE JSON line with the throughput, the roofline of the attention
+kernel (its own launches timed with HIP events on the stream it runs on),
+a sampled parity check against the oracle, and the oracle's own throughput
+on a bounded sample on the host cores (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s on 1 MI355X and % of bf16 MFMA peak; ms per DiT attention call"
+PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PROFILE_GLOB = os.path.join(ROOT, "profiles", "*traffic*.md")
+KERNEL = "attn_fwd_bf16_kernel"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "video_diffusion_transformer_rope3d_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload_name: str):
+    """HBM bytes per attention launch from a committed rocprofv3 counter
+    summary, if it was taken on the current kernel source and workload."""
+    src = kernel_source_hash()
+    for p in glob.glob(PROFILE_GLOB):
+        text = open(p).read()
+        m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+        m_wl = re.search(r"workload:\s*(\S+)", text)
+        m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+        if m_src and m_b and m_wl and m_src.group(1) == src and m_wl.group(1) == workload_name:
+            return float(m_b.group(1))
+    return None
+
+
+def cpu_baseline(wl, host, budget_s: float):
+    """The oracle as it stands, on sampled query rows of whole (b, head)
+    slices (every key), for about ``budget_s`` seconds of host time."""
+    import numpy as np
+    import oracle
+    import workloads as wlmod
+    from threadpoolctl import threadpool_info
+
+    cores = len(os.sched_getaffinity(0))
+    dec = oracle.decode_bf16 if wl.dtype == "bf16" else (lambda a: a.astype(np.float64))
+    slices, rows_total, t_total = 0, 0, 0.0
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.heads)]
+    for (b, h) in pairs:
+        rows = wlmod.sample_rows(wl, b, h)
+        q, k, v = (dec(host[n][b, h]) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        oracle.rope_attention(q, k, v, wl.grid, wl.split, wl.theta, wl.scale, rows=rows)
+        t_total += time.perf_counter() - t0
+        slices += 1
+        rows_total += rows.size
+        if t_total >= budget_s:
+            break
+    flops = 4.0 * rows_total * wl.N * wl.d
+    blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas[0]) if blas else cores,
+        "kind": "oracle",
+        "sample": f"{slices} (b, head) slices x {rows_total // max(slices, 1)} sampled query rows against all "
+                  f"{wl.N} keys (fp64 NumPy, keys rotated in full per slice); {t_total:.1f} s; "
+                  f"{cores} host cores available",
+        "seconds": t_total,
+        "ms_per_call_extrapolated": t_total / rows_total * wl.N * wl.B * wl.heads * 1e3,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="host time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention path has no multi-GPU mode "
+              "(each GPU would hold its own (batch, head) share); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import video_diffusion_transformer_rope3d_amd as va
+    import workloads as wlmod
+
+    wl = wlmod.WORKLOADS[args.workload]
+    assert wl.dtype == "bf16", "the benchmark workload is a bf16 one"
+    t0 = time.time()
+    host = {n: wlmod.full(wl, n) for n in ("q", "k", "v")}
+    print(f"# inputs generated in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(host[n].view(np.int16)).to(dev).view(torch.bfloat16) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    ws = va.workspace_for(q, True)
+    rope = dict(grid=wl.grid, split=wl.split, theta=wl.theta)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def fused():
+        va.attention(q, k, v, scale=wl.scale, out=o, workspace=ws, stream=stream, **rope)
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K fused calls
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fused()
+        ev[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per_call = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---- the two kernels apart: pre-pass and attention launches, same stream
+    def timed(fn, n):
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in es:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in es]
+
+    prep_ms = timed(lambda: va.prepare(k, v, workspace=ws, stream=stream, **rope), args.steps)
+    attn_ms = timed(lambda: va.attend(q, k, v, ws, scale=wl.scale, out=o, stream=stream, **rope), args.steps)
+    attn_mean = statistics.mean(attn_ms)
+    achieved = wl.flops / (attn_mean * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {**wl.describe(), "qk_mfma": "f16", "pv_mfma": "bf16", "flops_per_call": wl.flops},
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
+        "ms_per_call": {"mean": round(statistics.mean(per_call), 3), "median": round(statistics.median(per_call), 3),
+                        "min": round(min(per_call), 3)},
+        "breakdown_ms": {"kv_prepass": round(statistics.mean(prep_ms), 3), "attention_kernel": round(attn_mean, 3)},
+        "roofline": {"kernel": KERNEL, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": committed_traffic(wl.name)},
+    }
+
+    if not args.no_parity:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from tests import parity
+        st = parity.compare(wl, host, o, slices=[(0, 0), (wl.B - 1, wl.heads - 1)])
+        result["parity_sample"] = {k2: (round(v2, 7) if isinstance(v2, float) else v2) for k2, v2 in st.items()}
+        result["parity_sample"]["slices"] = "(0,0) and (B-1,heads-1), 256 rows each"
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

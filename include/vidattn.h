@@ -130,6 +130,31 @@ vidattn_status vidattn_fwd(const void* q, const void* k, const void* v, void* o,
                            const vidattn_rope3d_desc* rope, void* workspace, size_t workspace_bytes,
                            void* hip_stream);
 
+/* The two phases of vidattn_fwd, for callers that time them apart or attend
+ * several times against one key/value set.
+ *
+ * vidattn_fwd_prepare writes the key/value operand image into the
+ * workspace: for BF16 the rotated keys rounded to fp16 and a transposed copy
+ * of v, both tiled in matrix-core operand order; for F32 the rotated keys
+ * (nothing when rope is NULL). Arguments as for vidattn_fwd.
+ *
+ * vidattn_fwd_attend runs the attention kernel on q against a workspace
+ * that vidattn_fwd_prepare filled for the same dt, B, heads, N, d, rope and
+ * the same k, v contents (not checked: a workspace prepared from other
+ * arguments gives meaningless output). k and v must be the tensors given to
+ * vidattn_fwd_prepare; they are read only on the F32 path. The workspace is
+ * only read. Argument rules as for vidattn_fwd.
+ *
+ * vidattn_fwd(...) is vidattn_fwd_prepare(...) followed by
+ * vidattn_fwd_attend(...) on the same stream, bit for bit. */
+vidattn_status vidattn_fwd_prepare(const void* k, const void* v, vidattn_dtype dt, int64_t B, int64_t heads,
+                                   int64_t N, int64_t d, const vidattn_rope3d_desc* rope, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream);
+vidattn_status vidattn_fwd_attend(const void* q, const void* k, const void* v, const void* workspace, void* o,
+                                  vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                  float softmax_scale, const vidattn_rope3d_desc* rope, size_t workspace_bytes,
+                                  void* hip_stream);
+
 /* Workspace bytes vidattn_fwd needs for these sizes (0 if none). Returns 0
  * also for arguments vidattn_fwd would reject; a positive size never
  * depends on the data. BF16: the rotated fp16 keys and a transposed copy of

@@ -125,3 +125,32 @@ def test_rope_rejects(kw, status, needle):
 def test_last_error_is_per_call():
     fwd(q=None)
     assert va.vidattn_last_error() != ""
+
+
+def test_prepare_and_attend_reject():
+    wsb = va.vidattn_fwd_workspace_size(va.BF16, 2, 40, N5, 128, 1)
+    s = va.vidattn_fwd_prepare(K, V, va.BF16, 2, 40, N5, 128, GOOD, WS, wsb - 1)
+    assert s == 3 and "workspace" in va.vidattn_last_error()
+    s = va.vidattn_fwd_prepare(K, V, va.BF16, 2, 40, N5, 128, GOOD, K, wsb)
+    assert s == 1 and "overlaps" in va.vidattn_last_error()
+    s = va.vidattn_fwd_prepare(None, V, va.BF16, 2, 40, N5, 128, GOOD, WS, wsb)
+    assert s == 1
+    s = va.vidattn_fwd_attend(Q, K, V, WS, O, va.BF16, 2, 40, N5, 128, -1.0, GOOD, wsb)
+    assert s == 1 and "softmax_scale" in va.vidattn_last_error()
+    s = va.vidattn_fwd_attend(Q, K, V, None, O, va.BF16, 2, 40, N5, 128, 0.1, GOOD, wsb)
+    assert s == 3
+    s = va.vidattn_fwd_attend(Q, K, V, WS, WS, va.BF16, 2, 40, N5, 128, 0.1, GOOD, wsb)
+    assert s == 1 and "overlaps" in va.vidattn_last_error()
+    s = va.vidattn_fwd_attend(Q, K, V, WS, O, va.BF16, 2, 40, N5 + 1, 128, 0.1, GOOD, wsb)
+    assert s == 1 and "does not equal N" in va.vidattn_last_error()
+
+
+def test_single_hip_runtime_whatever_the_import_order():
+    """Importing the binding before torch must not map a second HIP runtime
+    (torch bundles its own libamdhip64 under the system soname)."""
+    import subprocess
+    import sys
+    code = ("import video_diffusion_transformer_rope3d_amd as va, torch; "
+            "r = va._loaded_hip_runtimes(); print(len(r)); assert len(r) == 1, r")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]

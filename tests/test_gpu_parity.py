@@ -203,3 +203,19 @@ def test_error_status_raises(va):
     with pytest.raises(va.VidattnError) as e:
         va.attention(q, q.clone(), q.clone())
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
+def test_two_phase_equals_fused_bitwise(va, dt, rope):
+    wl = wlmod.custom(2, 3, (3, 11, 17), 128, (44, 42, 42), dtype=dt, seed_id=600)
+    host = parity.host_inputs(wl)
+    q, k, v = (parity.to_torch(host[n]) for n in ("q", "k", "v"))
+    kw = dict(grid=wl.grid, split=wl.split, theta=wl.theta) if rope else {}
+    fused = va.attention(q, k, v, **kw)
+    ws = va.prepare(k, v, **kw)
+    a1 = va.attend(q, k, v, ws, **kw)
+    a2 = va.attend(q, k, v, ws, **kw)  # the workspace is only read
+    torch.cuda.synchronize()
+    iv = torch.int16 if dt == "bf16" else torch.int32
+    assert torch.equal(fused.view(iv), a1.view(iv)) and torch.equal(a1.view(iv), a2.view(iv))

@@ -15,8 +15,8 @@ import os
 
 __all__ = [
     "BF16", "F16", "F32", "VidattnError", "Rope3dDesc", "lib_path", "load",
-    "vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_workspace_size", "vidattn_status_string",
-    "vidattn_last_error", "vidattn_abi_version", "attention", "rope3d", "workspace_for",
+    "vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend", "vidattn_fwd_workspace_size", "vidattn_status_string",
+    "vidattn_last_error", "vidattn_abi_version", "attention", "prepare", "attend", "rope3d", "workspace_for",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -24,8 +24,9 @@ BF16, F16, F32 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 ABI_VERSION = 1
 
-EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_workspace_size", "vidattn_status_string",
-                    "vidattn_last_error", "vidattn_abi_version")
+EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend",
+                    "vidattn_fwd_workspace_size", "vidattn_status_string", "vidattn_last_error",
+                    "vidattn_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -56,6 +57,20 @@ class Rope3dDesc(ctypes.Structure):
 _LIB = None
 
 
+def _loaded_hip_runtimes() -> set:
+    """Distinct libamdhip64 files mapped into this process."""
+    out = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and "libamdhip64" in parts[-1]:
+                    out.add(os.path.realpath(parts[-1]))
+    except OSError:
+        pass
+    return out
+
+
 def load() -> ctypes.CDLL:
     """Load libvidattn.so once; raises ImportError if it is not built."""
     global _LIB
@@ -64,8 +79,20 @@ def load() -> ctypes.CDLL:
     path = lib_path()
     if not os.path.exists(path):
         raise ImportError(f"libvidattn.so not found at {path}; build it with "
-                          "`python -m video_diffusion_transformer_rope3d_amd.build`")
+                          "`python video_diffusion_transformer_rope3d_amd/build.py`")
+    # PyTorch-ROCm bundles its own HIP runtime under the same soname as the
+    # system one. Loading torch first makes libvidattn bind to that copy, so
+    # the streams and device pointers torch hands over belong to the runtime
+    # that launches the kernels.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
+    runtimes = _loaded_hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process (" + ", ".join(sorted(runtimes)) +
+                          "); import torch before anything that loads /opt/rocm's libamdhip64")
     vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     lib.vidattn_rope3d.restype = ctypes.c_int
     lib.vidattn_rope3d.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64,
@@ -73,6 +100,12 @@ def load() -> ctypes.CDLL:
     lib.vidattn_fwd.restype = ctypes.c_int
     lib.vidattn_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                 ctypes.POINTER(Rope3dDesc), vp, sz, vp]
+    lib.vidattn_fwd_prepare.restype = ctypes.c_int
+    lib.vidattn_fwd_prepare.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.POINTER(Rope3dDesc), vp,
+                                        sz, vp]
+    lib.vidattn_fwd_attend.restype = ctypes.c_int
+    lib.vidattn_fwd_attend.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
+                                       ctypes.POINTER(Rope3dDesc), sz, vp]
     lib.vidattn_fwd_workspace_size.restype = sz
     lib.vidattn_fwd_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
     lib.vidattn_status_string.restype = ctypes.c_char_p
@@ -103,6 +136,17 @@ def vidattn_fwd(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, workspace, 
     return load().vidattn_fwd(q, k, v, o, dt, B, heads, N, d, softmax_scale,
                               ctypes.byref(rope) if rope is not None else None, workspace, workspace_bytes,
                               stream)
+
+
+def vidattn_fwd_prepare(k, v, dt, B, heads, N, d, rope, workspace, workspace_bytes, stream=None) -> int:
+    return load().vidattn_fwd_prepare(k, v, dt, B, heads, N, d, ctypes.byref(rope) if rope is not None else None,
+                                      workspace, workspace_bytes, stream)
+
+
+def vidattn_fwd_attend(q, k, v, workspace, o, dt, B, heads, N, d, softmax_scale, rope, workspace_bytes,
+                       stream=None) -> int:
+    return load().vidattn_fwd_attend(q, k, v, workspace, o, dt, B, heads, N, d, softmax_scale,
+                                     ctypes.byref(rope) if rope is not None else None, workspace_bytes, stream)
 
 
 def vidattn_fwd_workspace_size(dt, B, heads, N, d, use_rope) -> int:
@@ -163,22 +207,60 @@ def attention(q, k, v, *, scale=None, grid=None, split=None, theta=10000.0, out=
     With grid/split given, q and k are rotated by 3D RoPE inside the call;
     otherwise they are used as given."""
     B, H, N, d = q.shape
+    _check_qkv(q, k, v)
+    if out is None:
+        out = _torch().empty_like(q)
+    rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
+    if workspace is None:
+        workspace = workspace_for(q, rope is not None)
+    ws_ptr, ws_bytes = _ws(workspace)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _raise(vidattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(q), B, H, N, d, s, rope,
+                       ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def _check_qkv(q, k, v):
     for t in (k, v):
         if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
             raise ValueError("q, k, v must share shape, dtype and device")
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous [B, heads, N, d]")
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def prepare(k, v, *, grid=None, split=None, theta=10000.0, workspace=None, stream=None):
+    """First phase of ``attention``: write the key/value operand image of k,
+    v into a workspace (allocated if not given) and return it."""
+    _check_qkv(k, k, v)
+    B, H, N, d = k.shape
+    rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
+    if workspace is None:
+        workspace = workspace_for(k, rope is not None)
+    ptr, nbytes = _ws(workspace)
+    _raise(vidattn_fwd_prepare(k.data_ptr(), v.data_ptr(), _dt(k), B, H, N, d, rope, ptr, nbytes,
+                               _stream(stream)))
+    return workspace
+
+
+def attend(q, k, v, workspace, *, scale=None, grid=None, split=None, theta=10000.0, out=None, stream=None):
+    """Second phase of ``attention``: attention of q against the key/value
+    image ``prepare`` wrote for k, v with the same rotary arguments."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
     if out is None:
         out = _torch().empty_like(q)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
-    if workspace is None:
-        workspace = workspace_for(q, rope is not None)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ptr, nbytes = _ws(workspace)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _raise(vidattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(q), B, H, N, d, s, rope,
-                       ws_ptr, ws_bytes, _stream(stream)))
+    _raise(vidattn_fwd_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s,
+                              rope, nbytes, _stream(stream)))
     return out
 
 

@@ -1,6 +1,9 @@
 """Build libvidattn.so in-tree with hipcc for gfx950.
 
-    python -m video_diffusion_transformer_rope3d_amd.build
+    python video_diffusion_transformer_rope3d_amd/build.py
+
+(run by path: importing the package loads the library, which may not be
+built yet).
 
 Packed fp32 VALU instructions are disabled for all device code
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); hipcc's host pass

@@ -199,9 +199,17 @@ vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vi
   return ok();
 }
 
-vidattn_status vidattn_fwd(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,
-                           int64_t heads, int64_t N, int64_t d, float softmax_scale, const vidattn_rope3d_desc* rope,
-                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+enum class Phase { kFused, kPrepare, kAttend };
+
+// Shared argument checks of the three forward entry points; pointers that a
+// phase does not take are passed as a non-null placeholder.
+vidattn_status validate_fwd(Phase ph, const void* q, const void* k, const void* v, const void* o, vidattn_dtype dt,
+                            int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                            const vidattn_rope3d_desc* rope, const void* workspace, size_t workspace_bytes) {
   if (!q || !k || !v || !o) return fail(VIDATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(VIDATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
@@ -217,7 +225,7 @@ vidattn_status vidattn_fwd(const void* q, const void* k, const void* v, void* o,
     if (d & 1) return fail(VIDATTN_ERR_INVALID_ARG, "head dim %lld must be even", (long long)d);
     return fail(VIDATTN_ERR_UNSUPPORTED, "head dim %lld: supported are 64 and 128", (long long)d);
   }
-  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+  if (ph != Phase::kPrepare && (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)))
     return fail(VIDATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (rope)
     if (vidattn_status s = check_rope(rope, d, N, true)) return s;
@@ -229,73 +237,131 @@ vidattn_status vidattn_fwd(const void* q, const void* k, const void* v, void* o,
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(VIDATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   }
-  {
-    const int64_t tensor_bytes = nbh * N * d * (int64_t)dtype_size(dt);
+  const int64_t tensor_bytes = nbh * N * d * (int64_t)dtype_size(dt);
+  const char* w = static_cast<const char*>(workspace);
+  if (ph != Phase::kPrepare) {
     const char* ob = static_cast<const char*>(o);
     const char* ins[3] = {static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v)};
     for (const char* p : ins)
-      if (p < ob + tensor_bytes && ob < p + tensor_bytes)
-        return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps q, k or v");
-    if (need > 0) {
-      const char* w = static_cast<const char*>(workspace);
-      if (w < ob + tensor_bytes && ob < w + (int64_t)need) return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps the workspace");
-    }
+      if (p < ob + tensor_bytes && ob < p + tensor_bytes) return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps q, k or v");
+    if (need > 0 && w < ob + tensor_bytes && ob < w + (int64_t)need)
+      return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps the workspace");
   }
+  if (ph != Phase::kAttend && need > 0) {
+    const char* ins[2] = {static_cast<const char*>(k), static_cast<const char*>(v)};
+    for (const char* p : ins)
+      if (p < w + (int64_t)need && w < p + tensor_bytes)
+        return fail(VIDATTN_ERR_INVALID_ARG, "the workspace overlaps k or v");
+  }
+  if (dt == VIDATTN_BF16) {
+    const int64_t ntq = (N + kBR - 1) / kBR;
+    if (nbh * ntq > (int64_t)INT32_MAX / (kNW * 64))
+      return fail(VIDATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  } else {
+    const int64_t ntq = (N + 127) / 128;
+    if (nbh * ntq > (int64_t)INT32_MAX / 256) return fail(VIDATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  }
+  return VIDATTN_OK;
+}
 
-  const RopeParams rp = make_rope(rope);
-  const float log2e = 1.4426950408889634f;
-  const float qscale = softmax_scale * log2e;
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-
+// Launch the key/value pre-pass (arguments already validated).
+vidattn_status launch_prepare(const void* k, const void* v, vidattn_dtype dt, int64_t nbh, int64_t N, int64_t d,
+                              const RopeParams& rp, void* workspace, hipStream_t st) {
   if (dt == VIDATTN_BF16) {
     const int nkt = (int)((N + kKT - 1) / kKT);
     const int grp = bh_group(nkt, nbh);
     const dim3 pgrid((unsigned)nkt, (unsigned)((nbh + grp - 1) / grp));
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const int ntq = (int)((N + kBR - 1) / kBR);
-    const int64_t total = nbh * ntq;
-    if (total > (int64_t)INT32_MAX / (kNW * 64))
-      return fail(VIDATTN_ERR_UNSUPPORTED, "problem too large for one launch");
-    if (d == 128) {
+    if (d == 128)
       hipLaunchKernelGGL((prep_kv_kernel<128>), pgrid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp);
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, kNW, kQB>), dim3((unsigned)total), dim3(kNW * 64), 0, st,
-                         static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq,
-                         (int)total, qscale, rp);
-    } else {
+    else
       hipLaunchKernelGGL((prep_kv_kernel<64>), pgrid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp);
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, kNW, kQB>), dim3((unsigned)total), dim3(kNW * 64), 0, st,
-                         static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq,
-                         (int)total, qscale, rp);
-    }
-    if (vidattn_status s = hip_check("bf16 attention launch")) return s;
-    return ok();
+    return hip_check("bf16 key/value pre-pass launch");
   }
+  if (!rp.enabled) return VIDATTN_OK;
+  const int64_t xblocks = (N * (d / 8) + 255) / 256;
+  const int grp = bh_group(xblocks, nbh);
+  const dim3 grid((unsigned)xblocks, (unsigned)((nbh + grp - 1) / grp));
+  hipLaunchKernelGGL((rope3d_kernel<float, float>), grid, dim3(256), 0, st, static_cast<const float*>(k),
+                     static_cast<float*>(workspace), nbh, (int)N, (int)d, 1.0f, grp, rp);
+  return hip_check("f32 key rotation launch");
+}
 
-  // fp32
-  const float* kk = static_cast<const float*>(k);
-  if (rope) {
-    const int64_t items = N * (d / 8);
-    const int64_t xblocks = (items + 255) / 256;
-    const int grp = bh_group(xblocks, nbh);
-    const dim3 grid((unsigned)xblocks, (unsigned)((nbh + grp - 1) / grp));
-    hipLaunchKernelGGL((rope3d_kernel<float, float>), grid, dim3(256), 0, st, kk, static_cast<float*>(workspace), nbh,
-                       (int)N, (int)d, 1.0f, grp, rp);
-    kk = static_cast<const float*>(workspace);
+// Launch the attention kernel (arguments already validated).
+vidattn_status launch_attend(const void* q, const void* k, const void* v, const void* workspace, void* o,
+                             vidattn_dtype dt, int64_t nbh, int64_t N, int64_t d, float softmax_scale,
+                             const RopeParams& rp, hipStream_t st) {
+  const float log2e = 1.4426950408889634f;
+  const float qscale = softmax_scale * log2e;
+  if (dt == VIDATTN_BF16) {
+    const int nkt = (int)((N + kKT - 1) / kKT);
+    const int ntq = (int)((N + kBR - 1) / kBR);
+    const int total = (int)(nbh * ntq);
+    const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+    if (d == 128)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, kNW, kQB>), dim3((unsigned)total), dim3(kNW * 64), 0, st,
+                         static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq, total,
+                         qscale, rp);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, kNW, kQB>), dim3((unsigned)total), dim3(kNW * 64), 0, st,
+                         static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq, total,
+                         qscale, rp);
+    return hip_check("bf16 attention launch");
   }
+  const float* kk = rp.enabled ? static_cast<const float*>(workspace) : static_cast<const float*>(k);
   const int ntq = (int)((N + 127) / 128);
-  const int64_t total = nbh * ntq;
-  if (total > (int64_t)INT32_MAX / 256) return fail(VIDATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  const unsigned total = (unsigned)(nbh * ntq);
   if (d == 128)
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<128>), dim3((unsigned)total), dim3(256), 0, st,
-                       static_cast<const float*>(q), kk, static_cast<const float*>(v), static_cast<float*>(o), (int)N,
-                       ntq, qscale, rp);
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<128>), dim3(total), dim3(256), 0, st, static_cast<const float*>(q), kk,
+                       static_cast<const float*>(v), static_cast<float*>(o), (int)N, ntq, qscale, rp);
   else
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<64>), dim3((unsigned)total), dim3(256), 0, st,
-                       static_cast<const float*>(q), kk, static_cast<const float*>(v), static_cast<float*>(o), (int)N,
-                       ntq, qscale, rp);
-  if (vidattn_status s = hip_check("f32 attention launch")) return s;
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<64>), dim3(total), dim3(256), 0, st, static_cast<const float*>(q), kk,
+                       static_cast<const float*>(v), static_cast<float*>(o), (int)N, ntq, qscale, rp);
+  return hip_check("f32 attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+vidattn_status vidattn_fwd(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,
+                           int64_t heads, int64_t N, int64_t d, float softmax_scale, const vidattn_rope3d_desc* rope,
+                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (vidattn_status s = validate_fwd(Phase::kFused, q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, workspace,
+                                      workspace_bytes))
+    return s;
+  const RopeParams rp = make_rope(rope);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (vidattn_status s = launch_prepare(k, v, dt, B * heads, N, d, rp, workspace, st)) return s;
+  if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, B * heads, N, d, softmax_scale, rp, st)) return s;
+  return ok();
+}
+
+vidattn_status vidattn_fwd_prepare(const void* k, const void* v, vidattn_dtype dt, int64_t B, int64_t heads, int64_t N,
+                                   int64_t d, const vidattn_rope3d_desc* rope, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream) {
+  // q and o are not arguments of this phase: k stands in for both in the shared checks.
+  if (vidattn_status s = validate_fwd(Phase::kPrepare, k, k, v, k, dt, B, heads, N, d, 1.0f, rope, workspace,
+                                      workspace_bytes))
+    return s;
+  const RopeParams rp = make_rope(rope);
+  if (vidattn_status s = launch_prepare(k, v, dt, B * heads, N, d, rp, workspace, static_cast<hipStream_t>(hip_stream)))
+    return s;
+  return ok();
+}
+
+vidattn_status vidattn_fwd_attend(const void* q, const void* k, const void* v, const void* workspace, void* o,
+                                  vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                                  const vidattn_rope3d_desc* rope, size_t workspace_bytes, void* hip_stream) {
+  if (vidattn_status s = validate_fwd(Phase::kAttend, q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, workspace,
+                                      workspace_bytes))
+    return s;
+  const RopeParams rp = make_rope(rope);
+  if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, B * heads, N, d, softmax_scale, rp,
+                                       static_cast<hipStream_t>(hip_stream)))
+    return s;
   return ok();
 }
 
