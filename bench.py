@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s on 1 MI355X and % of bf16 MFMA peak; ms per DiT attention call"
 PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 PROFILE_GLOB = os.path.join(ROOT, "profiles", "*traffic*.md")
-KERNEL = "attn_fwd_bf16_kernel"
+KERNEL = "attn_fwd_bf16_pp_kernel"
 
 
 def kernel_source_hash() -> str:
@@ -104,6 +104,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="host time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before the timed region, run one plain device-to-device copy of this many MiB "
+                         "(a kernel of known traffic for scaling memory counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -130,6 +133,15 @@ def main() -> int:
     rope = dict(grid=wl.grid, split=wl.split, theta=wl.theta)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def fused():
         va.attention(q, k, v, scale=wl.scale, out=o, workspace=ws, stream=stream, **rope)

@@ -39,9 +39,11 @@ def command(out: str = LIB, extra=()) -> list:
             "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", out, *extra]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the library to ``out``; ``defines`` are extra -D options
+    (tile-shape knobs of the kernels)."""
+    tmp = out + ".tmp"
+    cmd = command(tmp, extra=[f"-D{d}" for d in defines])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,8 +52,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def assembly(out: str) -> None:

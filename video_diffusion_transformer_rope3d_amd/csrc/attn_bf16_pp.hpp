@@ -1,0 +1,360 @@
+// Flash-attention forward for bf16 Q/K/V on gfx950 matrix cores, with the
+// two waves of each SIMD in ping-pong.
+//
+// One workgroup = 8 waves (two per SIMD), 32 queries per wave, 256 queries
+// of one (batch, head) slice per workgroup. Keys and values stream through a
+// ring of NS LDS stages of KT = 64 keys, filled by direct global->LDS 16-byte
+// loads from the pre-pass workspace (already in matrix-core operand order:
+// every LDS read is one conflict-free ds_read_b128 per lane).
+//
+// Per wave and tile j there are two phases:
+//   GEMM_j     O^T += V_{j-1}^T P_{j-1}^T   (16 x v_mfma_f32_32x32x16_bf16)
+//              S'^T = K_j Q'^T - m          (16 x v_mfma_f32_32x32x16_f16)
+//   SOFTMAX_j  P_j = exp2(S'_j) -> bf16, row sums, rare exact rescale
+// Waves 0-3 (group A) and 4-7 (group B) sit one per SIMD each (the hardware
+// places wave w and w+4 of a workgroup on the same SIMD). One barrier opens
+// each tile period; in it group A runs GEMM then SOFTMAX and group B runs
+// SOFTMAX (of the previous tile) then GEMM, so on each SIMD one wave feeds
+// the matrix core while the other works on the vector ALU:
+//   period  0          1             2            ...  T
+//   A       G_0 S_0    G_1 S_1       G_2 S_2           G_T
+//   B       G_0        S_0 G_1       S_1 G_2           S_T-1 G_T
+// (G_T is the last P.V alone.) Stage s of the ring holds K_j and V_{j-1} for
+// j = s mod NS and is read in period j only; group A refills the stage of
+// tile j-1 with tile j+NS-1 during its GEMM of period j, spreading the
+// direct-to-LDS loads between MFMA batches.
+//
+// Numerics: the transposed products put all
+// scores and outputs of query q in lanes q and q+32, the running maximum m
+// enters as the accumulator input of the first score MFMA, and m moves only
+// when a tile's probability sum exceeds 2^20 (then the tile is redone against
+// the exact maximum and O, l are scaled).
+#pragma once
+
+#include <type_traits>
+
+// Where each wave issues its share of the ring refill: 1 = at the start of
+// its softmax phase, 0 = between the MFMA batches of its GEMM phase.
+#ifndef VIDATTN_BF16_FILL_IN_S
+#define VIDATTN_BF16_FILL_IN_S 1
+#endif
+
+#include "common.hpp"
+
+namespace vidattn {
+
+template <int D, int NS>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t* __restrict__ Q,
+                                                                  const uint8_t* __restrict__ ws,
+                                                                  uint16_t* __restrict__ O, int N, int nkt, int ntq,
+                                                                  int total_wg, float qscale, RopeParams rp) {
+  constexpr int NW = 8;
+  constexpr int KT = 64;
+  constexpr int BR = NW * 32;
+  constexpr int KSTEPS = D / 16;  // 16-wide head-dim steps of the score product
+  constexpr int DB = D / 32;      // 32-wide head-dim blocks of the output
+  constexpr int MS = KT / 16;     // 16-key steps of the P.V product
+  constexpr int TILE = KT * D * 2;  // bytes of one K tile (and of one V tile)
+  constexpr int STAGE = 2 * TILE;
+  constexpr int NLOADER = NW;                          // every wave takes a share of the ring refill
+  constexpr int STAGE_LOADS = STAGE / (NLOADER * 1024);  // 1 KB loads per loader wave per stage
+  static_assert(STAGE % (NLOADER * 1024) == 0, "stage must split into whole 1 KB wave loads");
+  static_assert(NS >= 2 && STAGE_LOADS * (NS - 2) < 64, "vmcnt range");
+  constexpr float kRescaleSum = 1048576.0f;  // 2^20
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = wave >> 2;  // 0: GEMM then softmax in each period, 1: the reverse
+  const int g = lane >> 5, qi = lane & 31;
+
+  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
+  // contiguous range of (bh, query tile) so the workgroups resident on one
+  // XCD share the same K/V stream in its L2.
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7, k8 = wg >> 3;
+  const int per = total_wg >> 3, rem = total_wg & 7;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + k8;
+  const int bh = logical / ntq;
+  const int qt = logical - bh * ntq;
+  const uint8_t* wsbh = ws + (int64_t)bh * nkt * STAGE;
+
+  // Fill the stage of tile j: K_j and V_{j-1} (blocks 0 .. STAGE/1024-1 of the
+  // stage; K first). Load r of wave w moves block r*NW + w. At the ends (no V_{-1}, no K_T) a neighbouring tile is
+  // copied into the unused half so that every stage costs each loader wave
+  // exactly STAGE_LOADS loads (the vmcnt arithmetic below relies on it).
+  auto issue_one = [&](int j, int r) __attribute__((always_inline)) {
+    constexpr int KBLK = TILE / 1024;
+    const int blk = r * NLOADER + wave;
+    uint8_t* st = lds + (j % NS) * STAGE;
+    const uint8_t* src = blk < KBLK ? wsbh + (int64_t)(j < nkt ? j : nkt - 1) * STAGE + blk * 1024
+                                    : wsbh + (int64_t)(j > 0 ? j - 1 : 0) * STAGE + TILE + (blk - KBLK) * 1024;
+    __builtin_amdgcn_global_load_lds(src + lane * 16, (__attribute__((address_space(3))) void*)(st + blk * 1024), 16,
+                                     0, 0);
+  };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < STAGE_LOADS; ++r) issue_one(j, r);
+  };
+
+  // ---- queries: rotate, pre-scale by scale*log2(e), round to fp16 (B operand).
+  // Their loads are issued before any tile load, so waiting for tile 0 covers them.
+  half8 qreg[KSTEPS];
+  {
+    const int q = qt * BR + wave * 32 + qi;
+    const uint16_t* qrow = Q + ((int64_t)bh * N + (q < N ? q : 0)) * D;
+    u32x4 raw[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * g);
+    for (int j = 0; j < NS - 1; ++j)
+      if (j <= nkt) issue(j);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      float x[8];
+      unpack_bf16x8(raw[s], x);
+      if (rp.enabled) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float c, sn;
+          rope_cos_sin(rp, q < N ? q : 0, 8 * s + 4 * g + j, c, sn);
+          rotate_pair(x[2 * j], x[2 * j + 1], c, sn);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qreg[s][j] = (_Float16)(q < N ? x[j] * qscale : 0.f);
+    }
+  }
+
+  f32x16 oacc[DB];
+  f32x16 negm;  // -m broadcast: accumulator input of the first score MFMA
+  f32x16 sacc[2];
+  bf16x8 pk[MS];
+  float m = 0.f, l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negm[i] = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+
+  // P = exp2(S') as bf16 B operands; returns the lane's partial sum of the
+  // rounded probabilities. Score register i of key block kb is key
+  // 32kb + 16(i/8) + 8g + i%8, so pk[ms] holds keys 16ms + 8g .. +7.
+  auto probs = [&]() __attribute__((always_inline)) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float part[MS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 p;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * h + j]);
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pp = {p[2 * j], p[2 * j + 1]};
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pp, one, acc, false);
+        }
+        part[2 * kb + h] = acc;
+        pk[2 * kb + h] = p;
+      }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+
+  constexpr int kWaitNewer = STAGE_LOADS * (NS - 2);
+  constexpr int kVmcntNewer = (kWaitNewer & 0xF) | ((kWaitNewer >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
+  const int tail = N - (nkt - 1) * KT;  // valid keys of the last tile, 1..KT
+
+  // Barrier that opens tile period i: tile i must have landed (a loader's
+  // loads of the newer tiles may stay in flight).
+  auto tile_barrier = [&](int i) __attribute__((always_inline)) {
+    if (i + NS - 2 <= nkt)
+      __builtin_amdgcn_s_waitcnt(kVmcntNewer);
+    else
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    lds_barrier();
+  };
+
+  // GEMM phase of tile jj: O^T += V_{jj-1}^T P^T (PV), S'^T = K_jj Q'^T - m (SC).
+  // The operands (16 B per lane each) stream from LDS in batches of RB,
+  // double-buffered in registers: batch b+1 is read while the MFMAs of
+  // batch b run, so each MFMA finds its operand already loaded.
+  constexpr int RB = 4;
+  auto gemm = [&](auto PV, auto SC, auto FILL, int jj) __attribute__((always_inline)) {
+    const int fill = jj + NS - 1;  // tile loaded into the ring when FILL (period jj fills tile jj+NS-1)
+    // one register holds this lane's address in the stage; the operand
+    // offsets (< 32 KB) then fit the ds_read immediate field
+    uint32_t sb = (uint32_t)(uintptr_t)(lds + (jj % NS) * STAGE + lane * 16);
+    asm volatile("" : "+v"(sb));
+    const uint8_t* st = (const uint8_t*)(__attribute__((address_space(3))) const uint8_t*)(uintptr_t)sb;
+    constexpr int NV = decltype(PV)::value ? DB * MS : 0;  // V^T operand blocks
+    constexpr int NK = decltype(SC)::value ? 2 * KSTEPS : 0;  // K operand blocks
+    constexpr int NOP = NV + NK;
+    static_assert(NOP % RB == 0, "operand batches");
+    // operand i < NV: V block (db, ms) = i; else K block (kb, s) = i - NV
+    auto addr = [&](int i) __attribute__((always_inline)) { return st + (i < NV ? TILE + i * 1024 : (i - NV) * 1024); };
+    u32x4 buf[2][RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) buf[0][r] = *reinterpret_cast<const u32x4*>(addr(r));
+#pragma unroll
+    for (int b = 0; b < NOP / RB; ++b) {
+      if (b + 1 < NOP / RB) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) buf[(b + 1) & 1][r] = *reinterpret_cast<const u32x4*>(addr((b + 1) * RB + r));
+      }
+      // the ring refill (group A only) rides in the MFMA shadow, spread over the batches
+      if constexpr (decltype(FILL)::value) {
+        constexpr int NB = NOP / RB;
+#pragma unroll
+        for (int r = b * STAGE_LOADS / NB; r < (b + 1) * STAGE_LOADS / NB; ++r) issue_one(fill, r);
+      }
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const int i = b * RB + r;
+        const u32x4 a = buf[b & 1][r];
+        if (i < NV) {
+          const int db = i / MS, ms = i % MS;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pk[ms], oacc[db], 0, 0, 0);
+        } else {
+          const int kb = (i - NV) / KSTEPS, s = (i - NV) % KSTEPS;
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), qreg[s],
+                                                            s == 0 ? negm : sacc[kb], 0, 0, 0);
+        }
+      }
+    }
+    // keep the batch structure: RB reads up front, then (RB reads, RB MFMAs) per batch
+#pragma unroll
+    for (int b = 0; b < NOP / RB; ++b) {
+      __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
+      if (b > 0) __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, STAGE_LOADS, 0);  // VMEM read (ring refill), if any
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+  };
+
+  // SOFTMAX phase of tile jj (in the last tile, keys past N get -inf).
+  auto softmax = [&](int jj) __attribute__((always_inline)) {
+    {
+      if (jj == nkt - 1 && tail < KT) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
+            if (key >= tail) sacc[kb][i] = -INFINITY;
+          }
+      }
+    }
+    float ls = probs();
+    if (__builtin_amdgcn_ballot_w64(jj == 0 || !(ls <= kRescaleSum)) != 0) {
+      // exact maximum of the tile (relative to the current m)
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = xor32_max(mx);
+      const float delta = jj == 0 ? mx : fmaxf(mx, 0.f);
+      const float alpha = jj == 0 ? 1.f : __builtin_amdgcn_exp2f(-delta);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m += delta;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = -m;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] -= delta;
+      ls = probs();
+    }
+    l += ls;
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  // One barrier per tile period i; within it group A runs GEMM_i then
+  // SOFTMAX_i and group B runs SOFTMAX_{i-1} then GEMM_i, so on every SIMD
+  // the matrix core and the vector ALU serve different waves. Group A refills
+  // the ring with tile i+NS-1 inside GEMM_i.
+  //   A: [b0] G_0 S_0 [b1] G_1 S_1 ... [b(T-1)] G_T-1 S_T-1 [bT] G_T(P.V)
+  //   B: [b0] G_0     [b1] S_0 G_1 ... [b(T-1)] S_T-2 G_T-1 [bT] S_T-1 G_T(P.V)
+  // Period i refills the ring with tile i+NS-1 while that is <= nkt (the
+  // "refill" loops below; the "drain" loops follow). With FILL_IN_S each wave
+  // issues its share at the start of its softmax phase, otherwise between the
+  // MFMA batches of its GEMM phase.
+  constexpr bool kFillInS = VIDATTN_BF16_FILL_IN_S != 0;
+  using FG = std::integral_constant<bool, !kFillInS>;  // GEMM carries the refill
+  auto sm = [&](auto FILL, int j, int fill_tile) __attribute__((always_inline)) {
+    if constexpr (kFillInS && decltype(FILL)::value) issue(fill_tile);
+    softmax(j);
+  };
+  tile_barrier(0);
+  if (group == 0) {  // period i: GEMM_i then SOFTMAX_i
+    if (NS - 1 <= nkt) {
+      gemm(F{}, T{}, FG{}, 0);
+      sm(T{}, 0, NS - 1);
+    } else {
+      gemm(F{}, T{}, F{}, 0);
+      sm(F{}, 0, 0);
+    }
+    int j = 1;
+    for (; j < nkt && j + NS - 1 <= nkt; ++j) {
+      tile_barrier(j);
+      gemm(T{}, T{}, FG{}, j);
+      sm(T{}, j, j + NS - 1);
+    }
+    for (; j < nkt; ++j) {
+      tile_barrier(j);
+      gemm(T{}, T{}, F{}, j);
+      sm(F{}, j, 0);
+    }
+    tile_barrier(nkt);
+    gemm(T{}, F{}, F{}, nkt);
+  } else {  // period i: SOFTMAX_{i-1} then GEMM_i (period 0: GEMM_0 only)
+    if (NS - 1 <= nkt) {
+      if constexpr (kFillInS) issue(NS - 1);
+      gemm(F{}, T{}, FG{}, 0);
+    } else {
+      gemm(F{}, T{}, F{}, 0);
+    }
+    int j = 1;
+    for (; j < nkt && j + NS - 1 <= nkt; ++j) {
+      tile_barrier(j);
+      sm(T{}, j - 1, j + NS - 1);
+      gemm(T{}, T{}, FG{}, j);
+    }
+    for (; j < nkt; ++j) {
+      tile_barrier(j);
+      sm(F{}, j - 1, 0);
+      gemm(T{}, T{}, F{}, j);
+    }
+    tile_barrier(nkt);
+    sm(F{}, nkt - 1, 0);
+    gemm(T{}, F{}, F{}, nkt);
+  }
+
+  // ---- epilogue: O = O^T / l, rounded to bf16.
+  // Output register i of lane (q, g) in head-dim block db is d = 32db + 8(i/4) + 4g + i%4.
+  const int q = qt * BR + wave * 32 + qi;
+  const float inv = 1.0f / xor32_sum(l);
+  if (q < N) {
+    uint16_t* orow = O + ((int64_t)bh * N + q) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        bf16x4 v;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = (__bf16)(oacc[db][4 * ib + jj] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * ib + 4 * g) = v;
+      }
+  }
+}
+
+}  // namespace vidattn

@@ -81,6 +81,22 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier without a memory fence. __syncthreads() also drains
+// every outstanding global load (vmcnt(0)), which would wait for the
+// direct-to-LDS prefetches of later pipeline stages too; callers wait with
+// an explicit, counted vmcnt for exactly the loads that must have landed.
+// The memory clobber keeps the compiler from moving LDS accesses across it,
+// and lgkmcnt(0) retires this wave's LDS reads before others may refill.
+// (The wait is the builtin, not inline asm, so the compiler's wait-count
+// tracking knows every LDS/scalar load has retired here.)
+__device__ __forceinline__ void lds_barrier() {
+  constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);  // lgkmcnt(0), vmcnt/expcnt untouched
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Row index permutation of a 32-row MFMA operand block: swaps bits 2 and 3.
 // Loading key rho(i) into A-operand row i of the 32x32x16 score product
 // makes the 8 scores a lane holds per 16-key step belong to 8 consecutive

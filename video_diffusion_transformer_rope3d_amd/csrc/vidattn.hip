@@ -8,7 +8,7 @@
 #include <string>
 
 #include "vidattn.h"
-#include "attn_bf16.hpp"
+#include "attn_bf16_pp.hpp"
 #include "attn_f32.hpp"
 #include "rope_kernels.hpp"
 
@@ -53,8 +53,14 @@ bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxBH = int64_t(1) << 20;
 
-constexpr int kKT = 64;  // keys per tile of the bf16 attention kernel
-constexpr int kNW = 8;   // waves per workgroup of the bf16 attention kernel
+// bf16 attention kernel: 8 waves of 32 queries per workgroup, a ring of
+// VIDATTN_BF16_NS LDS stages of 64 keys (compile-time tuning knobs, with
+// VIDATTN_BF16_FILL_IN_S in attn_bf16_pp.hpp).
+#ifndef VIDATTN_BF16_NS
+#define VIDATTN_BF16_NS 3
+#endif
+constexpr int kKT = 64;  // keys per tile
+constexpr int kNW = 8;   // waves per workgroup
 constexpr int kQB = 1;   // 32-query blocks per wave
 constexpr int kBR = kNW * kQB * 32;
 
@@ -301,12 +307,12 @@ vidattn_status launch_attend(const void* q, const void* k, const void* v, const 
     const int total = (int)(nbh * ntq);
     const uint8_t* ws = static_cast<const uint8_t*>(workspace);
     if (d == 128)
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, kNW, kQB>), dim3((unsigned)total), dim3(kNW * 64), 0, st,
-                         static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq, total,
+      hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<128, VIDATTN_BF16_NS>), dim3((unsigned)total), dim3(kNW * 64), 0,
+                         st, static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq, total,
                          qscale, rp);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, kNW, kQB>), dim3((unsigned)total), dim3(kNW * 64), 0, st,
-                         static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq, total,
+      hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<64, VIDATTN_BF16_NS>), dim3((unsigned)total), dim3(kNW * 64), 0,
+                         st, static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq, total,
                          qscale, rp);
     return hip_check("bf16 attention launch");
   }
