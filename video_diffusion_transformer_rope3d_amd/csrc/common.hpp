@@ -52,14 +52,16 @@ __device__ __forceinline__ int rope_pos(const RopeParams& rp, int n, int p) {
   return p < rp.pair_t ? f : (p < rp.pair_th ? y : x);
 }
 
-// cos/sin of the rotation angle of pair p of token n: the angle and its
-// cos/sin are evaluated in double precision and rounded once to fp32.
+// cos/sin of the rotation angle of pair p of token n. The angle pos*omega is
+// formed and reduced modulo 2*pi in double precision (|angle| < 2^24 here,
+// so the reduced value is exact to ~1e-11), rounded to fp32 in [-pi, pi],
+// and its cos/sin taken in fp32 (absolute error ~2e-7, far below the fp16 /
+// bf16 rounding of the rotated values and within the fp32 path's bounds).
 __device__ __forceinline__ void rope_cos_sin(const RopeParams& rp, int n, int p, float& c, float& s) {
   const double ang = (double)rope_pos(rp, n, p) * rp.omega[p];
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+  const double turns = rint(ang * 0.15915494309189535);  // nearest multiple of 2*pi
+  const float r = (float)fma(-turns, 6.283185307179586, ang);
+  sincosf(r, &s, &c);
 }
 
 // Rotate one pair in fp32: (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
