@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, links or
 executes anything under ``oracle/``; only the tests, the smoke check and the
 benchmark's CPU-baseline leg do. The oracle shares no code with the HIP path.
 
-``reference``  plain float64 NumPy definition (rotation, logits, softmax, P.V)
+``reference``  plain float64 NumPy definition (rotation, logits, softmax, P.V;
+               also the query-subset and block-sparse variants)
 ``brute``      an independent pure-Python twin (complex-number rotation,
                explicit loops, ``math.fsum``) for tiny inputs
 
@@ -21,6 +22,9 @@ from .reference import (  # noqa: F401
     grid_positions,
     pair_frequencies,
     rope3d,
+    block_sparse_attention,
+    block_sparse_mask,
     rope3d_at,
     rope_attention,
+    rope_attention_subset,
 )

@@ -56,3 +56,37 @@ def attend(qs, ks, vs, scale):
 
 def rope_attend(qs, ks, vs, grid, split, theta, scale):
     return attend(rope(qs, grid, split, theta), rope(ks, grid, split, theta), vs, scale)
+
+
+def rope_attend_subset(q, q_index, k, v, grid, split, theta, scale):
+    """Query-subset attention: query row r sits at token q_index[r] of the
+    grid and attends to every key; explicit loops and math.fsum."""
+    F, H, W = grid
+    pos = positions(F, H, W)
+    qr = [rotate_token(q[r], pos[q_index[r]], split, theta) for r in range(len(q))]
+    kr = [rotate_token(k[j], pos[j], split, theta) for j in range(len(k))]
+    return attend(qr, kr, v, scale)
+
+
+def block_sparse_attend(q, k, v, grid, split, theta, scale, kv_blocks, kv_count, q_block, k_block):
+    """Block-sparse attention: token i attends to token j only when j's key
+    block (j // k_block) is listed for i's query block (i // q_block) among
+    the first kv_count entries; a token with no listed key gets zeros. Keys
+    and queries are rotated first when grid is given."""
+    if grid is not None:
+        q = rope(q, grid, split, theta)
+        k = rope(k, grid, split, theta)
+    d_v = len(v[0])
+    out = []
+    for i in range(len(q)):
+        listed = set(kv_blocks[i // q_block][:kv_count[i // q_block]])
+        keys = [j for j in range(len(k)) if j // k_block in listed]
+        if not keys:
+            out.append([0.0] * d_v)
+            continue
+        s = [scale * math.fsum(a * b for a, b in zip(q[i], k[j])) for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        tot = math.fsum(e)
+        out.append([math.fsum(e[n] * v[j][c] for n, j in enumerate(keys)) / tot for c in range(d_v)])
+    return out

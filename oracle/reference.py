@@ -129,3 +129,70 @@ def rope_attention(q, k, v, grid, split, theta, scale, rows=None) -> np.ndarray:
         rows = np.asarray(rows)
         qr = rope3d_at(np.asarray(q)[rows], pos[rows], split, theta)
     return attention(qr, kr, v, scale)
+
+
+# ---------------------------------------------------------------- query subset (key/value-cache synchronisation)
+
+def rope_attention_subset(q, q_index, k, v, grid, split, theta, scale, rows=None) -> np.ndarray:
+    """Query-subset attention of one (batch, head) slice: query row r is the
+    token q_index[r] of the grid (its rotary position), and every row attends
+    to all N keys. This is the key/value-cache synchronisation of
+    Heterogeneous Step Allocation (its abstract on the paper listing
+    thelatestinai.com/papers/2606.17566): active tokens attend to the full
+    sequence. q is (Nq, d); k, v are (N, d)."""
+    pos = grid_positions(grid)
+    q_index = np.asarray(q_index, dtype=np.int64)
+    q = np.asarray(q, np.float64)
+    if rows is not None:
+        rows = np.asarray(rows)
+        q, q_index = q[rows], q_index[rows]
+    qr = rope3d_at(q, pos[q_index], split, theta)
+    kr = rope3d_at(k, pos, split, theta)
+    return attention(qr, kr, v, scale)
+
+
+# ---------------------------------------------------------------- block-sparse attention
+
+def block_sparse_mask(N: int, kv_blocks, kv_count, q_block: int, k_block: int) -> np.ndarray:
+    """Boolean (N, N) visibility of one (batch, head) slice: query token i
+    sees key token j when j's key block (j // k_block) is among the first
+    kv_count[i // q_block] entries of kv_blocks[i // q_block]."""
+    kv_blocks = np.asarray(kv_blocks, dtype=np.int64)
+    kv_count = np.asarray(kv_count, dtype=np.int64)
+    allowed = np.zeros((kv_count.shape[0], -(-N // k_block)), dtype=bool)
+    for i, c in enumerate(kv_count):
+        allowed[i, kv_blocks[i, :c]] = True
+    qi = np.arange(N) // q_block
+    kj = np.arange(N) // k_block
+    return allowed[qi][:, kj]
+
+
+def block_sparse_attention(q, k, v, grid, split, theta, scale, kv_blocks, kv_count, q_block=256, k_block=64,
+                           rows=None) -> np.ndarray:
+    """Block-sparse attention of one (batch, head) slice, the block-sparse
+    video-DiT attention of ScalingAttention and of Persistent Block-Sparse
+    Attention (their abstracts on thelatestinai.com/papers/2606.17566): the
+    logits of keys outside the listed blocks are -inf before the softmax. A
+    query whose block lists no key block has no attended key; its output is
+    defined as 0 (a reading: the pages leave that case open). q, k, v are
+    (N, d) before rotation; kv_blocks (nqb, max_blocks) and kv_count (nqb,)
+    are the lists of this slice."""
+    N = np.asarray(q).shape[0]
+    pos = grid_positions(grid) if grid is not None else None
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    if pos is not None:
+        q = rope3d_at(q, pos, split, theta)
+        k = rope3d_at(k, pos, split, theta)
+    vis = block_sparse_mask(N, kv_blocks, kv_count, q_block, k_block)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    out = np.zeros((rows.shape[0], v.shape[1]), dtype=np.float64)
+    for n, i in enumerate(rows):
+        seen = vis[i]
+        if not seen.any():
+            continue
+        s = float(scale) * (k[seen] @ q[i])
+        e = np.exp(s - s.max())
+        out[n] = (e / e.sum()) @ v[seen]
+    return out
