@@ -104,6 +104,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="host time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--variant", choices=("dense", "subset", "sparse"), default="dense",
+                    help="subset: a quarter of the query tokens attend to all keys; sparse: block-sparse lists "
+                         "(a band of 96 key blocks each side of the query block plus 96 global key blocks)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the timed region, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling memory counters)")
@@ -142,6 +145,9 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.variant != "dense":
+        return variant_bench(args, va, wl, host, q, k, v, ws, rope, stream)
 
     def fused():
         va.attention(q, k, v, scale=wl.scale, out=o, workspace=ws, stream=stream, **rope)
@@ -214,6 +220,96 @@ def main() -> int:
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
 
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
+    """One line for the query-subset or block-sparse attention on the same
+    workload: a call is the key/value pre-pass plus the variant's attention;
+    FLOPs count only the query-key pairs the variant visits."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wlmod
+
+    QB, KB = va.SPARSE_Q_BLOCK, va.SPARSE_K_BLOCK
+    if args.variant == "subset":
+        idx = wlmod.subset_index(wl, wl.N // 4)
+        q_sub = torch.from_numpy(np.ascontiguousarray(host["q"][:, :, idx]).view(np.int16)).cuda().view(torch.bfloat16)
+        idx_t = torch.from_numpy(idx).cuda()
+        o = torch.empty_like(q_sub)
+        flops = 4.0 * wl.B * wl.heads * len(idx) * wl.N * wl.d
+        attend = lambda: va.attend_subset(q_sub, idx_t, ws, wl.N, scale=wl.scale, out=o, stream=stream, **rope)
+        name = f"{wl.name}-subset{len(idx)}"
+        detail = {"active_queries": int(len(idx)), "selection": "seeded distinct tokens, a quarter of N"}
+    else:
+        blocks, count = wlmod.block_lists(wl, QB, KB, window=96, n_global=96)
+        rows_in = np.minimum(QB, wl.N - QB * np.arange(count.shape[-1]))
+        ksize = np.minimum(KB, wl.N - KB * np.arange(-(-wl.N // KB)))
+        keys = np.where(blocks >= 0, ksize[np.maximum(blocks, 0)], 0).sum(axis=-1)
+        flops = 4.0 * wl.d * float((rows_in[None, None, :] * keys).sum())
+        bt, ct = torch.from_numpy(blocks).cuda(), torch.from_numpy(count).cuda()
+        o = torch.empty_like(q)
+        attend = lambda: va.attend_block_sparse(q, ws, bt, ct, scale=wl.scale, out=o, stream=stream, **rope)
+        name = f"{wl.name}-blocksparse-w96g96"
+        detail = {"max_blocks": int(blocks.shape[-1]), "density": round(flops / wl.flops, 4),
+                  "lists": "band of 96 key blocks each side of the query block + 96 seeded global key blocks"}
+    prep = lambda: va.prepare(k, v, workspace=ws, stream=stream, **rope)
+
+    for _ in range(args.warmup):
+        prep()
+        attend()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        prep()
+        attend()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in es:
+        a.record(stream)
+        attend()
+        b.record(stream)
+    torch.cuda.synchronize()
+    attn_mean = statistics.mean(a.elapsed_time(b) for a, b in es)
+    achieved = flops / (attn_mean * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {**wl.describe(), "workload": name, "variant": args.variant, **detail, "flops_per_call": flops},
+        "breakdown_ms": {"attention_kernel": round(attn_mean, 3)},
+        "roofline": {"kernel": KERNEL, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_parity:
+        from threadpoolctl import threadpool_limits
+        dec = oracle.decode_bf16
+        worst = dict(max_abs=0.0, mean_rel=0.0)
+        for (b, h) in [(0, 0), (wl.B - 1, wl.heads - 1)]:
+            with threadpool_limits(16):
+                if args.variant == "subset":
+                    rows = np.sort(np.random.default_rng(b * 100 + h).choice(len(idx), size=256, replace=False))
+                    ref = oracle.rope_attention_subset(dec(host["q"][b, h][idx]), idx, dec(host["k"][b, h]),
+                                                       dec(host["v"][b, h]), wl.grid, wl.split, wl.theta, wl.scale,
+                                                       rows=rows)
+                else:
+                    rows = wlmod.sample_rows(wl, b, h)
+                    ref = oracle.block_sparse_attention(dec(host["q"][b, h]), dec(host["k"][b, h]),
+                                                        dec(host["v"][b, h]), wl.grid, wl.split, wl.theta, wl.scale,
+                                                        blocks[b, h], count[b, h], QB, KB, rows=rows)
+            got = oracle.decode_bf16(o[b, h, torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy()
+                                     .view(np.uint16))
+            e = np.abs(got - ref)
+            worst["max_abs"] = max(worst["max_abs"], float(e.max()))
+            worst["mean_rel"] = max(worst["mean_rel"], float(e.sum() / np.abs(ref).sum()))
+        result["parity_sample"] = {**{k2: round(v2, 7) for k2, v2 in worst.items()},
+                                   "slices": "(0,0) and (B-1,heads-1), 256 rows each"}
     print(json.dumps(result), flush=True)
     return 0
 

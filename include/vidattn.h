@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define VIDATTN_ABI_VERSION 1
+#define VIDATTN_ABI_VERSION 2
 
 typedef enum {
   VIDATTN_OK = 0,
@@ -102,8 +102,10 @@ typedef struct {
  *            is not.
  *   prescale multiplies every rotated element (1.0f = none); finite.
  *   d        even, a multiple of 8, at most 256.
- * The rotation is computed in fp32 from fp64-evaluated cos/sin rounded to
- * fp32, then multiplied by prescale and rounded to nearest-even to out_dt.
+ * The rotation is computed in fp32: the angle is formed and reduced modulo
+ * 2*pi in fp64, and its cos/sin are evaluated in fp32 (absolute error about
+ * 2e-7); the result is multiplied by prescale and rounded to nearest-even
+ * to out_dt.
  * Pointers must be 16-byte aligned. */
 vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt,
                               int64_t B, int64_t heads, int64_t d, const vidattn_rope3d_desc* rope,
@@ -154,6 +156,69 @@ vidattn_status vidattn_fwd_attend(const void* q, const void* k, const void* v, c
                                   vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
                                   float softmax_scale, const vidattn_rope3d_desc* rope, size_t workspace_bytes,
                                   void* hip_stream);
+
+/* Block sizes of the block-sparse attention below: queries are grouped in
+ * blocks of 256 tokens, keys in blocks of 64 tokens (the tiles of the bf16
+ * attention kernel). */
+#define VIDATTN_SPARSE_Q_BLOCK 256
+#define VIDATTN_SPARSE_K_BLOCK 64
+
+/* Query-subset attention against a prepared key/value set: Nq gathered
+ * query tokens attend to all N keys: the key/value-cache synchronisation of
+ * Heterogeneous Step Allocation (HSA; its abstract on the paper listing
+ * thelatestinai.com/papers/2606.17566), where the active tokens attend to
+ * the whole sequence (the page names the operation, not an interface). Same
+ * operation as
+ * vidattn_fwd_attend restricted to the rows q_index[0 .. Nq-1], for query
+ * rows supplied in that order.
+ *   q         [B][heads][Nq][d] BF16; row r is the query of token q_index[r].
+ *   q_index   int32 [Nq], device memory, shared by every (b, head): the
+ *             token index in [0, N) of each query row; it gives the row's
+ *             rotary position (frame, row, column under the token order
+ *             above). Repeated and unordered indices are allowed. Entries
+ *             outside [0, N) are clamped into it (the library does not read
+ *             the array on the host); callers must pass valid indices.
+ *   o         [B][heads][Nq][d] BF16.
+ *   workspace filled by vidattn_fwd_prepare for (BF16, B, heads, N, d, rope)
+ *             and the keys/values to attend; only read.
+ * With q_index = 0 .. N-1 and Nq = N the result is bit-identical to
+ * vidattn_fwd_attend. Only BF16 is implemented (F32: UNSUPPORTED). Pointers
+ * 16-byte aligned (q_index 4-byte); o must not overlap q or the workspace. */
+vidattn_status vidattn_fwd_attend_subset(const void* q, const int32_t* q_index, int64_t Nq, const void* workspace,
+                                         void* o, vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                         float softmax_scale, const vidattn_rope3d_desc* rope, size_t workspace_bytes,
+                                         void* hip_stream);
+
+/* Block-sparse attention against a prepared key/value set: each query block
+ * attends only to the key blocks listed for it: the block-sparse video-DiT
+ * attention of ScalingAttention (a bit-wise block-sparse kernel driven by a
+ * per-head block mask) and of Sparse Forcing's Persistent Block-Sparse
+ * Attention (their abstracts on the paper listing
+ * thelatestinai.com/papers/2606.17566). Logits of unlisted key blocks are
+ * -inf before the softmax; a query block with no listed key block gets O = 0
+ * (a reading: the pages do not define that case).
+ *   q, o        [B][heads][N][d] BF16.
+ *   kv_blocks   int32 [B][heads][ceil(N/256)][max_blocks], device memory:
+ *               for query block (b, head, i) (tokens 256i .. 256i+255) the
+ *               indices of its key blocks (tokens 64j .. 64j+63), strictly
+ *               ascending, in the first kv_count[b][head][i] entries; the
+ *               other entries are ignored.
+ *   kv_count    int32 [B][heads][ceil(N/256)], device memory, each in
+ *               [0, max_blocks].
+ *   max_blocks  in [1, ceil(N/64)].
+ *   workspace   as for vidattn_fwd_attend_subset.
+ * Counts and indices are not read on the host: counts outside [0,
+ * max_blocks] and indices outside [0, ceil(N/64)) are clamped into range,
+ * and the result for lists that are not strictly ascending is unspecified
+ * (but stays inside the buffers). Listing every key block gives the dense
+ * result bit for bit. Only BF16 is implemented (F32: UNSUPPORTED).
+ * Pointers 16-byte aligned (the two index arrays 4-byte); o must not overlap
+ * q or the workspace. */
+vidattn_status vidattn_fwd_attend_block_sparse(const void* q, const void* workspace, void* o, vidattn_dtype dt,
+                                               int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                                               const vidattn_rope3d_desc* rope, const int32_t* kv_blocks,
+                                               const int32_t* kv_count, int64_t max_blocks, size_t workspace_bytes,
+                                               void* hip_stream);
 
 /* Workspace bytes vidattn_fwd needs for these sizes (0 if none). Returns 0
  * also for arguments vidattn_fwd would reject; a positive size never

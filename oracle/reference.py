@@ -178,21 +178,27 @@ def block_sparse_attention(q, k, v, grid, split, theta, scale, kv_blocks, kv_cou
     (N, d) before rotation; kv_blocks (nqb, max_blocks) and kv_count (nqb,)
     are the lists of this slice."""
     N = np.asarray(q).shape[0]
-    pos = grid_positions(grid) if grid is not None else None
-    q = np.asarray(q, np.float64)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    q = np.asarray(q, np.float64)[rows]
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
-    if pos is not None:
-        q = rope3d_at(q, pos, split, theta)
+    if grid is not None:
+        pos = grid_positions(grid)
+        q = rope3d_at(q, pos[rows], split, theta)
         k = rope3d_at(k, pos, split, theta)
-    vis = block_sparse_mask(N, kv_blocks, kv_count, q_block, k_block)
-    rows = np.arange(N) if rows is None else np.asarray(rows)
+    # listed[i, c]: key block c is listed for query block i
+    kv_blocks = np.asarray(kv_blocks, dtype=np.int64)
+    kv_count = np.asarray(kv_count, dtype=np.int64)
+    listed = np.zeros((kv_count.shape[0], -(-N // k_block)), dtype=bool)
+    for i, c in enumerate(kv_count):
+        listed[i, kv_blocks[i, :c]] = True
+    key_block = np.arange(N) // k_block
     out = np.zeros((rows.shape[0], v.shape[1]), dtype=np.float64)
     for n, i in enumerate(rows):
-        seen = vis[i]
+        seen = listed[i // q_block][key_block]
         if not seen.any():
             continue
-        s = float(scale) * (k[seen] @ q[i])
+        s = float(scale) * (k[seen] @ q[n])
         e = np.exp(s - s.max())
         out[n] = (e / e.sum()) @ v[seen]
     return out

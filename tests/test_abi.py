@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_strings():
-    assert va.vidattn_abi_version() == 1
+    assert va.vidattn_abi_version() == 2
     for s, txt in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "workspace too small"),
                    (4, "HIP error")]:
         assert va.vidattn_status_string(s) == txt
@@ -143,6 +143,45 @@ def test_prepare_and_attend_reject():
     assert s == 1 and "overlaps" in va.vidattn_last_error()
     s = va.vidattn_fwd_attend(Q, K, V, WS, O, va.BF16, 2, 40, N5 + 1, 128, 0.1, GOOD, wsb)
     assert s == 1 and "does not equal N" in va.vidattn_last_error()
+
+
+QI, KB, KC = 6 * P, 7 * P, 8 * P  # fake index arrays
+T = 1 << 40  # fake, far-apart tensor addresses for full-size shapes
+QF, OF, WSF = T, 2 * T, 3 * T
+
+
+def test_attend_subset_rejects():
+    wsb = va.vidattn_fwd_workspace_size(va.BF16, 2, 40, N5, 128, 1)
+    sub = lambda **kw: va.vidattn_fwd_attend_subset(**{**dict(
+        q=QF, q_index=QI, Nq=1000, workspace=WSF, o=OF, dt=va.BF16, B=2, heads=40, N=N5, d=128, softmax_scale=0.1,
+        rope=GOOD, workspace_bytes=wsb), **kw})
+    assert sub(dt=va.F32) == 2
+    assert sub(q_index=None) == 1 and "q_index" in va.vidattn_last_error()
+    assert sub(q_index=QI + 2) == 1 and "aligned" in va.vidattn_last_error()
+    assert sub(Nq=0) == 1
+    assert sub(Nq=(1 << 24) + 1) == 2
+    assert sub(workspace_bytes=wsb - 1) == 3
+    assert sub(softmax_scale=float("nan")) == 1 and "softmax_scale" in va.vidattn_last_error()
+    assert sub(N=N5 + 1) == 1 and "does not equal N" in va.vidattn_last_error()
+    # o overlaps q only through the Nq rows it has: 2*40*1000*128*2 bytes
+    assert sub(o=QF + 2 * 40 * 1000 * 128 * 2 - 16) == 1 and "overlaps q" in va.vidattn_last_error()
+    assert sub(o=WSF) == 1 and "overlaps" in va.vidattn_last_error()
+
+
+def test_attend_block_sparse_rejects():
+    wsb = va.vidattn_fwd_workspace_size(va.BF16, 2, 40, N5, 128, 1)
+    nkb = -(-N5 // va.SPARSE_K_BLOCK)
+    bs = lambda **kw: va.vidattn_fwd_attend_block_sparse(**{**dict(
+        q=QF, workspace=WSF, o=OF, dt=va.BF16, B=2, heads=40, N=N5, d=128, softmax_scale=0.1, rope=GOOD,
+        kv_blocks=KB, kv_count=KC, max_blocks=16, workspace_bytes=wsb), **kw})
+    assert bs(dt=va.F32) == 2
+    assert bs(kv_blocks=None) == 1 and "kv_blocks" in va.vidattn_last_error()
+    assert bs(kv_count=KC + 1) == 1 and "aligned" in va.vidattn_last_error()
+    assert bs(max_blocks=0) == 1 and "max_blocks" in va.vidattn_last_error()
+    assert bs(max_blocks=nkb + 1) == 1 and "max_blocks" in va.vidattn_last_error()
+    assert bs(workspace_bytes=wsb - 1) == 3
+    assert bs(d=96) == 2
+    assert bs(o=QF) == 1 and "overlaps q" in va.vidattn_last_error()
 
 
 def test_single_hip_runtime_whatever_the_import_order():

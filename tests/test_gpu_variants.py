@@ -1,0 +1,267 @@
+"""Parity of the query-subset and block-sparse attention (HIP path through
+the C ABI) with the fp64 CPU oracle on the same seeded inputs, plus the
+identities that tie them to the dense attention. Needs an MI355X."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wlmod
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+QB, KB = 256, 64  # query / key block sizes of the block-sparse entry point
+
+
+@pytest.fixture(scope="module")
+def va():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import video_diffusion_transformer_rope3d_amd as m
+    assert (m.SPARSE_Q_BLOCK, m.SPARSE_K_BLOCK) == (QB, KB)
+    return m
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _prepare(va, wl, host, rope=True):
+    q, k, v = (parity.to_torch(host[n]) for n in ("q", "k", "v"))
+    kw = dict(grid=wl.grid, split=wl.split, theta=wl.theta) if rope else {}
+    ws = va.prepare(k, v, **kw)
+    return q, k, v, ws, kw
+
+
+def _stats(got, ref):
+    e = np.abs(got - ref)
+    sr = float(np.abs(ref).sum())
+    return dict(max_abs=float(e.max()) if e.size else 0.0, mean_rel=float(e.sum()) / sr if sr > 0 else 0.0,
+                finite=bool(np.all(np.isfinite(got))))
+
+
+def _within(st):
+    t = parity.TOL["bf16"]
+    return st["finite"] and st["max_abs"] <= t["max_abs"] and st["mean_rel"] <= t["mean_rel"]
+
+
+def _merge(parts):
+    return dict(max_abs=max(p["max_abs"] for p in parts), mean_rel=max(p["mean_rel"] for p in parts),
+                finite=all(p["finite"] for p in parts))
+
+
+# ------------------------------------------------------------------ query subset
+
+SUBSET_CASES = [
+    # grid, d, split, B, H, how the Nq query tokens are chosen
+    ((3, 11, 17), 128, (44, 42, 42), 2, 2, "random-with-repeats", 300),
+    ((3, 11, 17), 64, (16, 24, 24), 1, 3, "random-with-repeats", 257),
+    ((5, 13, 17), 128, (44, 42, 42), 1, 2, "distinct-ascending", 700),
+    ((2, 4, 8), 128, (44, 42, 42), 1, 1, "single", 1),
+    ((2, 9, 11), 128, (44, 42, 42), 2, 1, "more-rows-than-keys", 500),
+]
+
+
+def _subset_index(wl, how, nq, seed):
+    g = np.random.default_rng(seed)
+    if how == "distinct-ascending":
+        return np.sort(g.choice(wl.N, size=nq, replace=False)).astype(np.int32)
+    if how == "single":
+        return np.array([wl.N - 1], dtype=np.int32)
+    return g.integers(0, wl.N, size=nq).astype(np.int32)
+
+
+@pytest.mark.parametrize("case", SUBSET_CASES, ids=lambda c: f"{c[5]}-{c[0][0]}x{c[0][1]}x{c[0][2]}-d{c[1]}-nq{c[6]}")
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
+def test_subset_small(va, case, rope):
+    grid, d, split, B, H, how, nq = case
+    wl = wlmod.custom(B, H, grid, d, split, seed_id=600 + d + nq)
+    host = parity.host_inputs(wl)
+    idx = _subset_index(wl, how, nq, seed=nq)
+    _log(f"subset {wl.name} nq={nq} {how} rope={rope}")
+    _, _, _, ws, kw = _prepare(va, wl, host, rope)
+    q_sub = np.ascontiguousarray(host["q"][:, :, idx])
+    o = va.attend_subset(parity.to_torch(q_sub), torch.from_numpy(idx).cuda(), ws, wl.N, scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    got = parity.from_torch(o)
+    parts = []
+    for b in range(B):
+        for h in range(H):
+            qd, kd, vd = (parity.decode(wl, a) for a in (q_sub[b, h], host["k"][b, h], host["v"][b, h]))
+            if rope:
+                ref = oracle.rope_attention_subset(qd, idx, kd, vd, wl.grid, wl.split, wl.theta, wl.scale)
+            else:
+                ref = oracle.attention(qd, kd, vd, wl.scale)
+            parts.append(_stats(got[b, h], ref))
+    st = _merge(parts)
+    _log(f"  {st}")
+    assert _within(st), st
+
+
+def test_subset_identity_is_the_dense_attention_bitwise(va):
+    wl = wlmod.custom(2, 2, (3, 11, 17), 128, (44, 42, 42), seed_id=620)
+    host = parity.host_inputs(wl)
+    q, k, v, ws, kw = _prepare(va, wl, host)
+    idx = torch.arange(wl.N, dtype=torch.int32, device="cuda")
+    a = va.attend_subset(q, idx, ws, wl.N, scale=wl.scale, **kw)
+    b = va.attend(q, k, v, ws, scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_subset_rows_equal_gathered_dense_rows_bitwise(va):
+    """Each output row depends only on its query and its token index, so a
+    gathered subset reproduces the dense rows of those tokens bit for bit."""
+    wl = wlmod.custom(1, 2, (5, 13, 17), 128, (44, 42, 42), seed_id=621)
+    host = parity.host_inputs(wl)
+    q, k, v, ws, kw = _prepare(va, wl, host)
+    idx = wlmod.subset_index(wl, 333)
+    it = torch.from_numpy(idx).long().cuda()
+    a = va.attend_subset(q[:, :, it].contiguous(), it.int(), ws, wl.N, scale=wl.scale, **kw)
+    dense = va.attend(q, k, v, ws, scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), dense[:, :, it].contiguous().view(torch.int16))
+
+
+def test_subset_large(va):
+    """The 32760-token grid with a quarter of the tokens active; every active
+    row of two (b, head) slices is checked against the oracle."""
+    wl = wlmod.WORKLOADS[2]
+    host = parity.host_inputs(wl)
+    idx = wlmod.subset_index(wl, 8190)
+    _log(f"subset {wl.name} nq={len(idx)}")
+    _, _, _, ws, kw = _prepare(va, wl, host)
+    q_sub = np.ascontiguousarray(host["q"][:, :, idx])
+    o = va.attend_subset(parity.to_torch(q_sub), torch.from_numpy(idx).cuda(), ws, wl.N, scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(len(idx), size=256, replace=False))
+    parts = []
+    for (b, h) in [(0, 0), (wl.B - 1, wl.heads - 1)]:
+        got = parity.from_torch(o[b, h, torch.from_numpy(rows).cuda()])
+        qd, kd, vd = (parity.decode(wl, a) for a in (q_sub[b, h], host["k"][b, h], host["v"][b, h]))
+        ref = oracle.rope_attention_subset(qd, idx, kd, vd, wl.grid, wl.split, wl.theta, wl.scale, rows=rows)
+        parts.append(_stats(got, ref))
+    st = _merge(parts)
+    _log(f"  {st}")
+    assert _within(st), st
+
+
+# ------------------------------------------------------------------ block sparse
+
+def _random_lists(wl, seed, max_blocks, empty_every=0):
+    """Ascending lists of random length (0 .. max_blocks), the last key block
+    (the ragged one) always among the candidates."""
+    g = np.random.default_rng(seed)
+    nqb, nkb = -(-wl.N // QB), -(-wl.N // KB)
+    blocks = np.full((wl.B, wl.heads, nqb, max_blocks), -1, dtype=np.int32)
+    count = np.zeros((wl.B, wl.heads, nqb), dtype=np.int32)
+    for b in range(wl.B):
+        for h in range(wl.heads):
+            for i in range(nqb):
+                c = int(g.integers(1, max_blocks + 1))
+                if empty_every and (b * wl.heads + h + i) % empty_every == 0:
+                    c = 0
+                sel = np.sort(g.choice(nkb, size=min(c, nkb), replace=False))
+                blocks[b, h, i, :len(sel)] = sel
+                count[b, h, i] = len(sel)
+    return blocks, count
+
+
+def _check_sparse(va, wl, host, blocks, count, rope=True, rows=None, slices=None):
+    q, _, _, ws, kw = _prepare(va, wl, host, rope)
+    o = va.attend_block_sparse(q, ws, torch.from_numpy(blocks).cuda(), torch.from_numpy(count).cuda(),
+                               scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    parts = []
+    for (b, h) in (slices or [(b, h) for b in range(wl.B) for h in range(wl.heads)]):
+        r = np.arange(wl.N) if rows is None else rows
+        got = parity.from_torch(o[b, h, torch.from_numpy(r).cuda()])
+        qd, kd, vd = (parity.decode(wl, host[n][b, h]) for n in ("q", "k", "v"))
+        ref = oracle.block_sparse_attention(qd, kd, vd, wl.grid if rope else None, wl.split, wl.theta, wl.scale,
+                                            blocks[b, h], count[b, h], QB, KB, rows=r)
+        # query blocks without keys must be exactly zero
+        empty = count[b, h][r // QB] == 0
+        assert np.all(got[empty] == 0.0)
+        parts.append(_stats(got, ref))
+    return o, _merge(parts)
+
+
+SPARSE_CASES = [
+    # grid, d, split, B, H, max listed key blocks, every n-th query block empty (0: none)
+    ((3, 11, 17), 128, (44, 42, 42), 2, 2, 4, 0),
+    ((3, 11, 17), 64, (16, 24, 24), 1, 3, 9, 3),
+    ((5, 13, 17), 128, (44, 42, 42), 1, 2, 6, 4),
+    ((2, 9, 11), 128, (44, 42, 42), 2, 1, 1, 0),
+    ((4, 8, 8), 128, (44, 42, 42), 1, 2, 3, 0),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=lambda c: f"{c[0][0]}x{c[0][1]}x{c[0][2]}-d{c[1]}-max{c[5]}")
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
+def test_sparse_small(va, case, rope):
+    grid, d, split, B, H, maxb, empty_every = case
+    wl = wlmod.custom(B, H, grid, d, split, seed_id=640 + d + maxb)
+    host = parity.host_inputs(wl)
+    blocks, count = _random_lists(wl, seed=maxb + d, max_blocks=min(maxb, -(-wl.N // KB)), empty_every=empty_every)
+    _log(f"sparse {wl.name} max_blocks={blocks.shape[-1]} rope={rope}")
+    _, st = _check_sparse(va, wl, host, blocks, count, rope)
+    _log(f"  {st}")
+    assert _within(st), st
+
+
+def test_sparse_window_and_global_blocks(va):
+    """Lists of the kind the pages describe (a local band around the query
+    block plus a persistent global set), on a grid of 7 query blocks."""
+    wl = wlmod.custom(2, 2, (4, 15, 29), 128, (44, 42, 42), seed_id=660)
+    host = parity.host_inputs(wl)
+    blocks, count = wlmod.block_lists(wl, QB, KB, window=2, n_global=3)
+    _log(f"sparse {wl.name} window lists max={blocks.shape[-1]}")
+    _, st = _check_sparse(va, wl, host, blocks, count)
+    _log(f"  {st}")
+    assert _within(st), st
+
+
+def test_sparse_all_blocks_is_the_dense_attention_bitwise(va):
+    wl = wlmod.custom(2, 2, (3, 11, 17), 128, (44, 42, 42), seed_id=661)
+    host = parity.host_inputs(wl)
+    q, k, v, ws, kw = _prepare(va, wl, host)
+    nqb, nkb = -(-wl.N // QB), -(-wl.N // KB)
+    blocks = torch.arange(nkb, dtype=torch.int32, device="cuda").repeat(wl.B, wl.heads, nqb, 1).contiguous()
+    count = torch.full((wl.B, wl.heads, nqb), nkb, dtype=torch.int32, device="cuda")
+    a = va.attend_block_sparse(q, ws, blocks, count, scale=wl.scale, **kw)
+    b = va.attend(q, k, v, ws, scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_sparse_out_of_range_counts_and_indices_are_clamped(va):
+    """Counts above max_blocks act as max_blocks and an index past the last
+    key block acts as the last key block: same bits as the clamped lists."""
+    wl = wlmod.custom(1, 2, (3, 11, 17), 128, (44, 42, 42), seed_id=662)
+    host = parity.host_inputs(wl)
+    q, _, _, ws, kw = _prepare(va, wl, host)
+    nqb, nkb = -(-wl.N // QB), -(-wl.N // KB)
+    clean = np.tile(np.array([0, 3, nkb - 1], dtype=np.int32), (wl.B, wl.heads, nqb, 1))
+    dirty = clean.copy()
+    dirty[..., 2] = 1 << 20
+    cnt = np.full((wl.B, wl.heads, nqb), 3, dtype=np.int32)
+    over = np.full((wl.B, wl.heads, nqb), 1 << 30, dtype=np.int32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    a = va.attend_block_sparse(q, ws, t(clean), t(cnt), scale=wl.scale, **kw)
+    b = va.attend_block_sparse(q, ws, t(dirty), t(over), scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_sparse_large(va):
+    """The 32760-token grid (128 query blocks, 512 key blocks) with local
+    band + global lists; 256 sampled rows of two slices."""
+    wl = wlmod.WORKLOADS[2]
+    host = parity.host_inputs(wl)
+    blocks, count = wlmod.block_lists(wl, QB, KB, window=16, n_global=32)
+    rows = wlmod.sample_rows(wl, 0, 0)
+    _log(f"sparse {wl.name} window=16 global=32 max={blocks.shape[-1]}")
+    _, st = _check_sparse(va, wl, host, blocks, count, rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)])
+    _log(f"  {st}")
+    assert _within(st), st

@@ -15,16 +15,20 @@ import os
 
 __all__ = [
     "BF16", "F16", "F32", "VidattnError", "Rope3dDesc", "lib_path", "load",
-    "vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend", "vidattn_fwd_workspace_size", "vidattn_status_string",
-    "vidattn_last_error", "vidattn_abi_version", "attention", "prepare", "attend", "rope3d", "workspace_for",
-    "EXPORTED_SYMBOLS",
+    "vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend", "vidattn_fwd_attend_subset",
+    "vidattn_fwd_attend_block_sparse", "vidattn_fwd_workspace_size", "vidattn_status_string",
+    "vidattn_last_error", "vidattn_abi_version", "attention", "prepare", "attend", "attend_subset",
+    "attend_block_sparse", "rope3d", "workspace_for", "SPARSE_Q_BLOCK", "SPARSE_K_BLOCK", "EXPORTED_SYMBOLS",
 ]
 
 BF16, F16, F32 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 1
+ABI_VERSION = 2
+
+SPARSE_Q_BLOCK, SPARSE_K_BLOCK = 256, 64  # VIDATTN_SPARSE_Q_BLOCK, VIDATTN_SPARSE_K_BLOCK
 
 EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend",
+                    "vidattn_fwd_attend_subset", "vidattn_fwd_attend_block_sparse",
                     "vidattn_fwd_workspace_size", "vidattn_status_string", "vidattn_last_error",
                     "vidattn_abi_version")
 
@@ -106,6 +110,12 @@ def load() -> ctypes.CDLL:
     lib.vidattn_fwd_attend.restype = ctypes.c_int
     lib.vidattn_fwd_attend.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                        ctypes.POINTER(Rope3dDesc), sz, vp]
+    lib.vidattn_fwd_attend_subset.restype = ctypes.c_int
+    lib.vidattn_fwd_attend_subset.argtypes = [vp, vp, i64, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
+                                              ctypes.POINTER(Rope3dDesc), sz, vp]
+    lib.vidattn_fwd_attend_block_sparse.restype = ctypes.c_int
+    lib.vidattn_fwd_attend_block_sparse.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
+                                                    ctypes.POINTER(Rope3dDesc), vp, vp, i64, sz, vp]
     lib.vidattn_fwd_workspace_size.restype = sz
     lib.vidattn_fwd_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
     lib.vidattn_status_string.restype = ctypes.c_char_p
@@ -147,6 +157,20 @@ def vidattn_fwd_attend(q, k, v, workspace, o, dt, B, heads, N, d, softmax_scale,
                        stream=None) -> int:
     return load().vidattn_fwd_attend(q, k, v, workspace, o, dt, B, heads, N, d, softmax_scale,
                                      ctypes.byref(rope) if rope is not None else None, workspace_bytes, stream)
+
+
+def vidattn_fwd_attend_subset(q, q_index, Nq, workspace, o, dt, B, heads, N, d, softmax_scale, rope, workspace_bytes,
+                              stream=None) -> int:
+    return load().vidattn_fwd_attend_subset(q, q_index, Nq, workspace, o, dt, B, heads, N, d, softmax_scale,
+                                            ctypes.byref(rope) if rope is not None else None, workspace_bytes,
+                                            stream)
+
+
+def vidattn_fwd_attend_block_sparse(q, workspace, o, dt, B, heads, N, d, softmax_scale, rope, kv_blocks, kv_count,
+                                    max_blocks, workspace_bytes, stream=None) -> int:
+    return load().vidattn_fwd_attend_block_sparse(q, workspace, o, dt, B, heads, N, d, softmax_scale,
+                                                  ctypes.byref(rope) if rope is not None else None, kv_blocks,
+                                                  kv_count, max_blocks, workspace_bytes, stream)
 
 
 def vidattn_fwd_workspace_size(dt, B, heads, N, d, use_rope) -> int:
@@ -261,6 +285,51 @@ def attend(q, k, v, workspace, *, scale=None, grid=None, split=None, theta=10000
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s,
                               rope, nbytes, _stream(stream)))
+    return out
+
+
+def attend_subset(q, q_index, workspace, N, *, scale=None, grid=None, split=None, theta=10000.0, out=None,
+                  stream=None):
+    """Query-subset attention: the Nq rows of q (tokens ``q_index``, an int32
+    device tensor of Nq entries in [0, N)) attend to all N keys of the
+    key/value image ``prepare`` wrote (BF16)."""
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    if q_index.dtype != torch.int32 or q_index.dim() != 1 or q_index.numel() != Nq or not q_index.is_contiguous():
+        raise ValueError("q_index must be a contiguous int32 vector with one entry per query row")
+    if out is None:
+        out = torch.empty_like(q)
+    rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
+    ptr, nbytes = _ws(workspace)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _raise(vidattn_fwd_attend_subset(q.data_ptr(), q_index.data_ptr(), Nq, ptr, out.data_ptr(), _dt(q), B, H, N, d,
+                                     s, rope, nbytes, _stream(stream)))
+    return out
+
+
+def attend_block_sparse(q, workspace, kv_blocks, kv_count, *, scale=None, grid=None, split=None, theta=10000.0,
+                        out=None, stream=None):
+    """Block-sparse attention: query block i (tokens 256i..256i+255) of each
+    (b, head) attends only to the key blocks (64 tokens each) listed in
+    ``kv_blocks[b, head, i, :kv_count[b, head, i]]`` (int32 device tensors of
+    shapes [B, heads, ceil(N/256), max_blocks] and [B, heads, ceil(N/256)])."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    nqb = -(-N // SPARSE_Q_BLOCK)
+    if kv_blocks.dtype != torch.int32 or kv_count.dtype != torch.int32:
+        raise ValueError("kv_blocks and kv_count must be int32")
+    if kv_blocks.dim() != 4 or tuple(kv_blocks.shape[:3]) != (B, H, nqb) or not kv_blocks.is_contiguous():
+        raise ValueError(f"kv_blocks must be a contiguous [{B}, {H}, {nqb}, max_blocks] tensor")
+    if tuple(kv_count.shape) != (B, H, nqb) or not kv_count.is_contiguous():
+        raise ValueError(f"kv_count must be a contiguous [{B}, {H}, {nqb}] tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
+    ptr, nbytes = _ws(workspace)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _raise(vidattn_fwd_attend_block_sparse(q.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s, rope,
+                                           kv_blocks.data_ptr(), kv_count.data_ptr(), kv_blocks.shape[3], nbytes,
+                                           _stream(stream)))
     return out
 
 

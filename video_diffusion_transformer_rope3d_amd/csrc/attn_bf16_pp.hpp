@@ -29,6 +29,15 @@
 // enters as the accumulator input of the first score MFMA, and m moves only
 // when a tile's probability sum exceeds 2^20 (then the tile is redone against
 // the exact maximum and O, l are scaled).
+//
+// Two variants share the loop. Query subset: Nq query rows (Nq may differ
+// from the Nk keys) whose rotary positions are the token indices qidx[row]
+// (qidx == nullptr: row r is token r). Block-sparse (SPARSE): each
+// (b, head, 256-query block) visits only the 64-key tiles listed in
+// kvb[.][0 .. kvc[.]-1] (ascending), so "tile j" of the loop is the j-th
+// listed tile; a block with no listed tile gets O = 0. Indices read from
+// device memory are clamped into range, so no input can address outside the
+// workspace.
 #pragma once
 
 #include <type_traits>
@@ -43,11 +52,11 @@
 
 namespace vidattn {
 
-template <int D, int NS>
-__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t* __restrict__ Q,
-                                                                  const uint8_t* __restrict__ ws,
-                                                                  uint16_t* __restrict__ O, int N, int nkt, int ntq,
-                                                                  int total_wg, float qscale, RopeParams rp) {
+template <int D, int NS, bool SPARSE>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
+    const uint16_t* __restrict__ Q, const uint8_t* __restrict__ ws, uint16_t* __restrict__ O, int N, int nkt, int Nq,
+    int ntq, int total_wg, float qscale, RopeParams rp, const int32_t* __restrict__ qidx,
+    const int32_t* __restrict__ kvb, const int32_t* __restrict__ kvc, int maxb) {
   constexpr int NW = 8;
   constexpr int KT = 64;
   constexpr int BR = NW * 32;
@@ -79,16 +88,45 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t
   const int qt = logical - bh * ntq;
   const uint8_t* wsbh = ws + (int64_t)bh * nkt * STAGE;
 
-  // Fill the stage of tile j: K_j and V_{j-1} (blocks 0 .. STAGE/1024-1 of the
-  // stage; K first). Load r of wave w moves block r*NW + w. At the ends (no V_{-1}, no K_T) a neighbouring tile is
-  // copied into the unused half so that every stage costs each loader wave
-  // exactly STAGE_LOADS loads (the vmcnt arithmetic below relies on it).
+  // Key tiles this workgroup visits: all nkt (dense) or its list (SPARSE).
+  // Loop position j maps to workspace tile tile_at(j), clamped into range.
+  const int32_t* lst = SPARSE ? kvb + ((int64_t)bh * ntq + qt) * maxb : nullptr;
+  int nt = nkt;
+  if constexpr (SPARSE) {
+    const int c = kvc[(int64_t)bh * ntq + qt];
+    nt = c < 0 ? 0 : (c > maxb ? maxb : c);
+  }
+  auto tile_at = [&](int j) __attribute__((always_inline)) {
+    j = j < 0 ? 0 : (j < nt ? j : nt - 1);
+    if constexpr (SPARSE) {
+      const int t = lst[j];
+      return t < 0 ? 0 : (t < nkt ? t : nkt - 1);
+    } else {
+      return j;
+    }
+  };
+  if (SPARSE && nt == 0) {  // no key visited: O = 0 for the block's rows
+    const int q = qt * BR + wave * 32 + qi;
+    if (q < Nq) {
+      uint16_t* orow = O + ((int64_t)bh * Nq + q) * D;
+#pragma unroll
+      for (int c = 0; c < D / 8; c += 2)
+        *reinterpret_cast<u32x4*>(orow + 8 * (c + g)) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+
+  // Fill the stage of loop tile j: K of tile j and V of tile j-1 (blocks
+  // 0 .. STAGE/1024-1 of the stage; K first). Load r of wave w moves block
+  // r*NW + w. At the ends (no V_{-1}, no K_nt) a neighbouring tile is copied
+  // into the unused half so that every stage costs each loader wave exactly
+  // STAGE_LOADS loads (the vmcnt arithmetic below relies on it).
   auto issue_one = [&](int j, int r) __attribute__((always_inline)) {
     constexpr int KBLK = TILE / 1024;
     const int blk = r * NLOADER + wave;
     uint8_t* st = lds + (j % NS) * STAGE;
-    const uint8_t* src = blk < KBLK ? wsbh + (int64_t)(j < nkt ? j : nkt - 1) * STAGE + blk * 1024
-                                    : wsbh + (int64_t)(j > 0 ? j - 1 : 0) * STAGE + TILE + (blk - KBLK) * 1024;
+    const uint8_t* src = blk < KBLK ? wsbh + (int64_t)tile_at(j) * STAGE + blk * 1024
+                                    : wsbh + (int64_t)tile_at(j - 1) * STAGE + TILE + (blk - KBLK) * 1024;
     __builtin_amdgcn_global_load_lds(src + lane * 16, (__attribute__((address_space(3))) void*)(st + blk * 1024), 16,
                                      0, 0);
   };
@@ -102,12 +140,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t
   half8 qreg[KSTEPS];
   {
     const int q = qt * BR + wave * 32 + qi;
-    const uint16_t* qrow = Q + ((int64_t)bh * N + (q < N ? q : 0)) * D;
+    const uint16_t* qrow = Q + ((int64_t)bh * Nq + (q < Nq ? q : 0)) * D;
     u32x4 raw[KSTEPS];
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * g);
+    // rotary position of this row: its token index in the grid
+    int pos = q < Nq ? q : 0;
+    if (qidx) {
+      const int t = qidx[pos];
+      pos = t < 0 ? 0 : (t < N ? t : N - 1);
+    }
     for (int j = 0; j < NS - 1; ++j)
-      if (j <= nkt) issue(j);
+      if (j <= nt) issue(j);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       float x[8];
@@ -116,12 +160,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float c, sn;
-          rope_cos_sin(rp, q < N ? q : 0, 8 * s + 4 * g + j, c, sn);
+          rope_cos_sin(rp, pos, 8 * s + 4 * g + j, c, sn);
           rotate_pair(x[2 * j], x[2 * j + 1], c, sn);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qreg[s][j] = (_Float16)(q < N ? x[j] * qscale : 0.f);
+      for (int j = 0; j < 8; ++j) qreg[s][j] = (_Float16)(q < Nq ? x[j] * qscale : 0.f);
     }
   }
 
@@ -166,12 +210,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t
   constexpr int kWaitNewer = STAGE_LOADS * (NS - 2);
   constexpr int kVmcntNewer = (kWaitNewer & 0xF) | ((kWaitNewer >> 4) << 14) | (0x7 << 4) | (0xF << 8);
   constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
-  const int tail = N - (nkt - 1) * KT;  // valid keys of the last tile, 1..KT
+  const int tail = N - (nkt - 1) * KT;  // valid keys of the last key tile, 1..KT
 
   // Barrier that opens tile period i: tile i must have landed (a loader's
   // loads of the newer tiles may stay in flight).
   auto tile_barrier = [&](int i) __attribute__((always_inline)) {
-    if (i + NS - 2 <= nkt)
+    if (i + NS - 2 <= nt)
       __builtin_amdgcn_s_waitcnt(kVmcntNewer);
     else
       __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -238,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t
   // SOFTMAX phase of tile jj (in the last tile, keys past N get -inf).
   auto softmax = [&](int jj) __attribute__((always_inline)) {
     {
-      if (jj == nkt - 1 && tail < KT) {
+      if (tail < KT && tile_at(jj) == nkt - 1) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -296,7 +340,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t
   };
   tile_barrier(0);
   if (group == 0) {  // period i: GEMM_i then SOFTMAX_i
-    if (NS - 1 <= nkt) {
+    if (NS - 1 <= nt) {
       gemm(F{}, T{}, FG{}, 0);
       sm(T{}, 0, NS - 1);
     } else {
@@ -304,47 +348,47 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(const uint16_t
       sm(F{}, 0, 0);
     }
     int j = 1;
-    for (; j < nkt && j + NS - 1 <= nkt; ++j) {
+    for (; j < nt && j + NS - 1 <= nt; ++j) {
       tile_barrier(j);
       gemm(T{}, T{}, FG{}, j);
       sm(T{}, j, j + NS - 1);
     }
-    for (; j < nkt; ++j) {
+    for (; j < nt; ++j) {
       tile_barrier(j);
       gemm(T{}, T{}, F{}, j);
       sm(F{}, j, 0);
     }
-    tile_barrier(nkt);
-    gemm(T{}, F{}, F{}, nkt);
+    tile_barrier(nt);
+    gemm(T{}, F{}, F{}, nt);
   } else {  // period i: SOFTMAX_{i-1} then GEMM_i (period 0: GEMM_0 only)
-    if (NS - 1 <= nkt) {
+    if (NS - 1 <= nt) {
       if constexpr (kFillInS) issue(NS - 1);
       gemm(F{}, T{}, FG{}, 0);
     } else {
       gemm(F{}, T{}, F{}, 0);
     }
     int j = 1;
-    for (; j < nkt && j + NS - 1 <= nkt; ++j) {
+    for (; j < nt && j + NS - 1 <= nt; ++j) {
       tile_barrier(j);
       sm(T{}, j - 1, j + NS - 1);
       gemm(T{}, T{}, FG{}, j);
     }
-    for (; j < nkt; ++j) {
+    for (; j < nt; ++j) {
       tile_barrier(j);
       sm(F{}, j - 1, 0);
       gemm(T{}, T{}, F{}, j);
     }
-    tile_barrier(nkt);
-    sm(F{}, nkt - 1, 0);
-    gemm(T{}, F{}, F{}, nkt);
+    tile_barrier(nt);
+    sm(F{}, nt - 1, 0);
+    gemm(T{}, F{}, F{}, nt);
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16.
   // Output register i of lane (q, g) in head-dim block db is d = 32db + 8(i/4) + 4g + i%4.
   const int q = qt * BR + wave * 32 + qi;
   const float inv = 1.0f / xor32_sum(l);
-  if (q < N) {
-    uint16_t* orow = O + ((int64_t)bh * N + q) * D;
+  if (q < Nq) {
+    uint16_t* orow = O + ((int64_t)bh * Nq + q) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -215,18 +215,23 @@ enum class Phase { kFused, kPrepare, kAttend };
 // phase does not take are passed as a non-null placeholder.
 vidattn_status validate_fwd(Phase ph, const void* q, const void* k, const void* v, const void* o, vidattn_dtype dt,
                             int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
-                            const vidattn_rope3d_desc* rope, const void* workspace, size_t workspace_bytes) {
+                            const vidattn_rope3d_desc* rope, const void* workspace, size_t workspace_bytes,
+                            int64_t Nq = -1) {
+  if (Nq < 0) Nq = N;  // rows of q and o (a query subset may have fewer or more than the N keys)
   if (!q || !k || !v || !o) return fail(VIDATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(VIDATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   if (dt != VIDATTN_BF16 && dt != VIDATTN_F32)
     return fail(dt == VIDATTN_F16 ? VIDATTN_ERR_UNSUPPORTED : VIDATTN_ERR_INVALID_ARG,
                 "attention dtype must be BF16 or F32");
-  if (B < 1 || heads < 1 || N < 1 || d < 1) return fail(VIDATTN_ERR_INVALID_ARG, "B, heads, N and d must be >= 1");
+  if (B < 1 || heads < 1 || N < 1 || d < 1 || Nq < 1)
+    return fail(VIDATTN_ERR_INVALID_ARG, "B, heads, N, Nq and d must be >= 1");
   int64_t nbh;
   if (!mul_ok(B, heads, &nbh) || nbh > kMaxBH)
     return fail(VIDATTN_ERR_INVALID_ARG, "B*heads overflows or exceeds %lld", (long long)kMaxBH);
-  if (N > kMaxN) return fail(VIDATTN_ERR_UNSUPPORTED, "N = %lld exceeds %lld", (long long)N, (long long)kMaxN);
+  if (N > kMaxN || Nq > kMaxN)
+    return fail(VIDATTN_ERR_UNSUPPORTED, "N = %lld or Nq = %lld exceeds %lld", (long long)N, (long long)Nq,
+                (long long)kMaxN);
   if (d != 64 && d != 128) {
     if (d & 1) return fail(VIDATTN_ERR_INVALID_ARG, "head dim %lld must be even", (long long)d);
     return fail(VIDATTN_ERR_UNSUPPORTED, "head dim %lld: supported are 64 and 128", (long long)d);
@@ -244,13 +249,17 @@ vidattn_status validate_fwd(Phase ph, const void* q, const void* k, const void* 
       return fail(VIDATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   }
   const int64_t tensor_bytes = nbh * N * d * (int64_t)dtype_size(dt);
+  const int64_t qo_bytes = nbh * Nq * d * (int64_t)dtype_size(dt);
   const char* w = static_cast<const char*>(workspace);
   if (ph != Phase::kPrepare) {
     const char* ob = static_cast<const char*>(o);
-    const char* ins[3] = {static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v)};
-    for (const char* p : ins)
-      if (p < ob + tensor_bytes && ob < p + tensor_bytes) return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps q, k or v");
-    if (need > 0 && w < ob + tensor_bytes && ob < w + (int64_t)need)
+    const char* qb = static_cast<const char*>(q);
+    if (qb < ob + qo_bytes && ob < qb + qo_bytes) return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps q");
+    const char* kv[2] = {static_cast<const char*>(k), static_cast<const char*>(v)};
+    for (const char* p : kv)
+      if (p != qb && p < ob + qo_bytes && ob < p + tensor_bytes)
+        return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps k or v");
+    if (need > 0 && w < ob + qo_bytes && ob < w + (int64_t)need)
       return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps the workspace");
   }
   if (ph != Phase::kAttend && need > 0) {
@@ -260,7 +269,7 @@ vidattn_status validate_fwd(Phase ph, const void* q, const void* k, const void* 
         return fail(VIDATTN_ERR_INVALID_ARG, "the workspace overlaps k or v");
   }
   if (dt == VIDATTN_BF16) {
-    const int64_t ntq = (N + kBR - 1) / kBR;
+    const int64_t ntq = (Nq + kBR - 1) / kBR;
     if (nbh * ntq > (int64_t)INT32_MAX / (kNW * 64))
       return fail(VIDATTN_ERR_UNSUPPORTED, "problem too large for one launch");
   } else {
@@ -296,24 +305,47 @@ vidattn_status launch_prepare(const void* k, const void* v, vidattn_dtype dt, in
 }
 
 // Launch the attention kernel (arguments already validated).
+// Optional inputs of the bf16 attention: a query subset (Nq rows with their
+// token indices) and a block-sparse key-tile list.
+struct AttendExtras {
+  int64_t Nq = -1;  // -1: Nq = N
+  const int32_t* qidx = nullptr;
+  const int32_t* kvb = nullptr;
+  const int32_t* kvc = nullptr;
+  int maxb = 0;
+};
+
+template <int D, bool SPARSE>
+void launch_bf16(const void* q, const uint8_t* ws, void* o, int N, int nkt, int Nq, int ntq, int total, float qscale,
+                 const RopeParams& rp, const AttendExtras& x, hipStream_t st) {
+  hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<D, VIDATTN_BF16_NS, SPARSE>), dim3((unsigned)total), dim3(kNW * 64), 0,
+                     st, static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), N, nkt, Nq, ntq, total,
+                     qscale, rp, x.qidx, x.kvb, x.kvc, x.maxb);
+}
+
 vidattn_status launch_attend(const void* q, const void* k, const void* v, const void* workspace, void* o,
                              vidattn_dtype dt, int64_t nbh, int64_t N, int64_t d, float softmax_scale,
-                             const RopeParams& rp, hipStream_t st) {
+                             const RopeParams& rp, hipStream_t st, const AttendExtras& x = AttendExtras{}) {
   const float log2e = 1.4426950408889634f;
   const float qscale = softmax_scale * log2e;
   if (dt == VIDATTN_BF16) {
+    const int64_t Nq = x.Nq < 0 ? N : x.Nq;
     const int nkt = (int)((N + kKT - 1) / kKT);
-    const int ntq = (int)((N + kBR - 1) / kBR);
+    const int ntq = (int)((Nq + kBR - 1) / kBR);
     const int total = (int)(nbh * ntq);
     const uint8_t* ws = static_cast<const uint8_t*>(workspace);
-    if (d == 128)
-      hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<128, VIDATTN_BF16_NS>), dim3((unsigned)total), dim3(kNW * 64), 0,
-                         st, static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq, total,
-                         qscale, rp);
-    else
-      hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<64, VIDATTN_BF16_NS>), dim3((unsigned)total), dim3(kNW * 64), 0,
-                         st, static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), (int)N, nkt, ntq, total,
-                         qscale, rp);
+    const bool sparse = x.kvb != nullptr;
+    if (d == 128) {
+      if (sparse)
+        launch_bf16<128, true>(q, ws, o, (int)N, nkt, (int)Nq, ntq, total, qscale, rp, x, st);
+      else
+        launch_bf16<128, false>(q, ws, o, (int)N, nkt, (int)Nq, ntq, total, qscale, rp, x, st);
+    } else {
+      if (sparse)
+        launch_bf16<64, true>(q, ws, o, (int)N, nkt, (int)Nq, ntq, total, qscale, rp, x, st);
+      else
+        launch_bf16<64, false>(q, ws, o, (int)N, nkt, (int)Nq, ntq, total, qscale, rp, x, st);
+    }
     return hip_check("bf16 attention launch");
   }
   const float* kk = rp.enabled ? static_cast<const float*>(workspace) : static_cast<const float*>(k);
@@ -367,6 +399,59 @@ vidattn_status vidattn_fwd_attend(const void* q, const void* k, const void* v, c
   const RopeParams rp = make_rope(rope);
   if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, B * heads, N, d, softmax_scale, rp,
                                        static_cast<hipStream_t>(hip_stream)))
+    return s;
+  return ok();
+}
+
+vidattn_status vidattn_fwd_attend_subset(const void* q, const int32_t* q_index, int64_t Nq, const void* workspace,
+                                         void* o, vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                         float softmax_scale, const vidattn_rope3d_desc* rope, size_t workspace_bytes,
+                                         void* hip_stream) {
+  if (dt != VIDATTN_BF16)
+    return fail(dt == VIDATTN_F32 || dt == VIDATTN_F16 ? VIDATTN_ERR_UNSUPPORTED : VIDATTN_ERR_INVALID_ARG,
+                "query-subset attention is implemented for BF16");
+  if (!q_index || (reinterpret_cast<uintptr_t>(q_index) & 3u) != 0)
+    return fail(VIDATTN_ERR_INVALID_ARG, "q_index must be non-null and 4-byte aligned");
+  // k and v are not arguments of this phase: q stands in for both in the shared checks.
+  if (vidattn_status s = validate_fwd(Phase::kAttend, q, q, q, o, dt, B, heads, N, d, softmax_scale, rope, workspace,
+                                      workspace_bytes, Nq))
+    return s;
+  const RopeParams rp = make_rope(rope);
+  AttendExtras x;
+  x.Nq = Nq;
+  x.qidx = q_index;
+  if (vidattn_status s = launch_attend(q, q, q, workspace, o, dt, B * heads, N, d, softmax_scale, rp,
+                                       static_cast<hipStream_t>(hip_stream), x))
+    return s;
+  return ok();
+}
+
+vidattn_status vidattn_fwd_attend_block_sparse(const void* q, const void* workspace, void* o, vidattn_dtype dt,
+                                               int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                                               const vidattn_rope3d_desc* rope, const int32_t* kv_blocks,
+                                               const int32_t* kv_count, int64_t max_blocks, size_t workspace_bytes,
+                                               void* hip_stream) {
+  if (dt != VIDATTN_BF16)
+    return fail(dt == VIDATTN_F32 || dt == VIDATTN_F16 ? VIDATTN_ERR_UNSUPPORTED : VIDATTN_ERR_INVALID_ARG,
+                "block-sparse attention is implemented for BF16");
+  if (!kv_blocks || !kv_count || (reinterpret_cast<uintptr_t>(kv_blocks) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(kv_count) & 3u) != 0)
+    return fail(VIDATTN_ERR_INVALID_ARG, "kv_blocks and kv_count must be non-null and 4-byte aligned");
+  if (vidattn_status s = validate_fwd(Phase::kAttend, q, q, q, o, dt, B, heads, N, d, softmax_scale, rope, workspace,
+                                      workspace_bytes))
+    return s;
+  const int64_t nkb = (N + VIDATTN_SPARSE_K_BLOCK - 1) / VIDATTN_SPARSE_K_BLOCK;
+  if (max_blocks < 1 || max_blocks > nkb)
+    return fail(VIDATTN_ERR_INVALID_ARG, "max_blocks = %lld must be in [1, ceil(N/%d) = %lld]", (long long)max_blocks,
+                VIDATTN_SPARSE_K_BLOCK, (long long)nkb);
+  static_assert(VIDATTN_SPARSE_K_BLOCK == kKT && VIDATTN_SPARSE_Q_BLOCK == kBR, "block sizes are the kernel's tiles");
+  const RopeParams rp = make_rope(rope);
+  AttendExtras x;
+  x.kvb = kv_blocks;
+  x.kvc = kv_count;
+  x.maxb = (int)max_blocks;
+  if (vidattn_status s = launch_attend(q, q, q, workspace, o, dt, B * heads, N, d, softmax_scale, rp,
+                                       static_cast<hipStream_t>(hip_stream), x))
     return s;
   return ok();
 }

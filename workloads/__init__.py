@@ -37,7 +37,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # stream ids inside a workload's seed
-T_Q, T_K, T_V, T_PEAKY, T_ROWS = 0, 1, 2, 3, 4
+T_Q, T_K, T_V, T_PEAKY, T_ROWS, T_SUBSET, T_BLOCKS = 0, 1, 2, 3, 4, 5, 6
 TENSOR_IDS = {"q": T_Q, "k": T_K, "v": T_V}
 
 SAMPLE_ROWS = 256  # query rows per (b, head) checked on large workloads
@@ -201,3 +201,43 @@ def sample_rows(wl: Workload, b: int, h: int) -> np.ndarray:
 
 def slice_sha256(arr: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(arr).tobytes()).hexdigest()
+
+
+# ---------------------------------------------------------------- inputs of the attention variants
+
+def subset_index(wl: Workload, n_active: int) -> np.ndarray:
+    """Token indices of the active queries of a query-subset attention: a
+    seeded draw of ``n_active`` distinct tokens of the grid, ascending (the
+    tokens that still take a denoising step; the rest are skipped)."""
+    g = _rng(wl, T_SUBSET, 0, 0)
+    return np.sort(g.choice(wl.N, size=n_active, replace=False)).astype(np.int32)
+
+
+def block_lists(wl: Workload, q_block: int, k_block: int, window: int, n_global: int,
+                max_blocks: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded block-sparse key lists, one per (b, head, query block): the key
+    blocks whose tokens fall in a band of ``window`` key blocks around the
+    query block's tokens (a local neighbourhood in token order) plus
+    ``n_global`` key blocks drawn uniformly (a persistent salient set), as
+    ascending lists padded with -1. Returns (kv_blocks [B, heads, nqb,
+    max_blocks] int32, kv_count [B, heads, nqb] int32)."""
+    N = wl.N
+    nqb, nkb = -(-N // q_block), -(-N // k_block)
+    lists = []
+    for b in range(wl.B):
+        for h in range(wl.heads):
+            g = _rng(wl, T_BLOCKS, b, h)
+            glob = g.choice(nkb, size=min(n_global, nkb), replace=False)
+            for i in range(nqb):
+                c0 = (i * q_block) // k_block
+                c1 = min(nkb - 1, (min(N, (i + 1) * q_block) - 1) // k_block)
+                lo, hi = max(0, c0 - window), min(nkb - 1, c1 + window)
+                lists.append(np.union1d(np.arange(lo, hi + 1), glob))
+    width = max_blocks or max(len(x) for x in lists)
+    blocks = np.full((wl.B * wl.heads * nqb, width), -1, dtype=np.int32)
+    count = np.zeros(wl.B * wl.heads * nqb, dtype=np.int32)
+    for r, x in enumerate(lists):
+        x = x[:width]
+        blocks[r, :len(x)] = x
+        count[r] = len(x)
+    return blocks.reshape(wl.B, wl.heads, nqb, width), count.reshape(wl.B, wl.heads, nqb)
