@@ -5,7 +5,8 @@ executes anything under ``oracle/``; only the tests, the smoke check and the
 benchmark's CPU-baseline leg do. The oracle shares no code with the HIP path.
 
 ``reference``  plain float64 NumPy definition (rotation, logits, softmax, P.V;
-               also the query-subset and block-sparse variants)
+               also the query-subset, block-sparse and local-window
+               variants)
 ``brute``      an independent pure-Python twin (complex-number rotation,
                explicit loops, ``math.fsum``) for tiny inputs
 
@@ -27,4 +28,6 @@ from .reference import (  # noqa: F401
     rope3d_at,
     rope_attention,
     rope_attention_subset,
+    window_attention,
+    window_visible,
 )

@@ -90,3 +90,23 @@ def block_sparse_attend(q, k, v, grid, split, theta, scale, kv_blocks, kv_count,
         tot = math.fsum(e)
         out.append([math.fsum(e[n] * v[j][c] for n, j in enumerate(keys)) / tot for c in range(d_v)])
     return out
+
+
+def window_attend(q, k, v, grid, split, theta, scale, radius):
+    """Local-window attention with explicit loops: token i attends to the
+    tokens whose grid coordinates differ from its own by at most the radius
+    on every axis."""
+    F, H, W = grid
+    pos = positions(F, H, W)
+    qr = rope(q, grid, split, theta)
+    kr = rope(k, grid, split, theta)
+    d_v = len(v[0])
+    out = []
+    for i in range(len(qr)):
+        keys = [j for j in range(len(kr)) if all(abs(pos[i][a] - pos[j][a]) <= radius[a] for a in range(3))]
+        s = [scale * math.fsum(a * b for a, b in zip(qr[i], kr[j])) for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        tot = math.fsum(e)
+        out.append([math.fsum(e[n] * v[j][c] for n, j in enumerate(keys)) / tot for c in range(d_v)])
+    return out

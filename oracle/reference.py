@@ -202,3 +202,44 @@ def block_sparse_attention(q, k, v, grid, split, theta, scale, kv_blocks, kv_cou
         e = np.exp(s - s.max())
         out[n] = (e / e.sum()) @ v[seen]
     return out
+
+
+# ---------------------------------------------------------------- local-window attention
+
+def window_visible(grid, radius, rows=None) -> np.ndarray:
+    """Boolean (len(rows), N) visibility of a sliding 3D window: query token
+    at (f, y, x) sees key token (f', y', x') when |f - f'| <= r_f,
+    |y - y'| <= r_h and |x - x'| <= r_w (clipped at the grid border)."""
+    pos = grid_positions(grid)
+    rows = np.arange(pos.shape[0]) if rows is None else np.asarray(rows)
+    r = np.asarray(radius, dtype=np.int64)
+    diff = np.abs(pos[rows][:, None, :] - pos[None, :, :])  # (rows, N, 3)
+    return np.all(diff <= r[None, None, :], axis=2)
+
+
+def window_attention(q, k, v, grid, split, theta, scale, radius, rows=None, rope=True) -> np.ndarray:
+    """Local-window attention of one (batch, head) slice: each query attends
+    only to the keys inside a box of radii (r_f, r_h, r_w) around its own
+    grid position (the windowed-attention primitive of the vidax summary,
+    "3D RoPE, 3D VAEs, and flash attention", and the sliding local windows of
+    Sparse Forcing's abstract on thelatestinai.com/papers/2606.17566; the
+    pages give no window shape, a centred box clipped at the border is the
+    plainest reading). Every query sees at least itself."""
+    N = np.asarray(q).shape[0]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    q = np.asarray(q, np.float64)[rows]
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    if rope:
+        pos = grid_positions(grid)
+        q = rope3d_at(q, pos[rows], split, theta)
+        k = rope3d_at(k, pos, split, theta)
+    out = np.empty((rows.shape[0], v.shape[1]), dtype=np.float64)
+    for c0 in range(0, rows.shape[0], 256):
+        vis = window_visible(grid, radius, rows[c0:c0 + 256])
+        for n in range(vis.shape[0]):
+            seen = vis[n]
+            s = float(scale) * (k[seen] @ q[c0 + n])
+            e = np.exp(s - s.max())
+            out[c0 + n] = (e / e.sum()) @ v[seen]
+    return out

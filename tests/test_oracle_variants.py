@@ -198,3 +198,98 @@ def test_pins_catch(name):
         except (AssertionError, IndexError, ValueError):  # a pin that fails or cannot run on the mutant catches it
             caught.append(pin.__name__)
     assert caught, f"no pin catches: {name}"
+
+
+# ---------------------------------------------------------------- local window
+
+WIMPL = types.SimpleNamespace(window=reference.window_attention)
+
+
+def pin_window_large_radius_is_dense(impl):
+    q, k, v = _data(20)
+    _close(impl.window(q, k, v, GRID, SPLIT, THETA, SCALE, (GRID[0], GRID[1], GRID[2])),
+           reference.rope_attention(q, k, v, GRID, SPLIT, THETA, SCALE), 1e-14, "unbounded window == dense")
+
+
+def pin_window_zero_radius_is_identity_on_v(impl):
+    q, k, v = _data(21)
+    _close(impl.window(q, k, v, GRID, SPLIT, THETA, SCALE, (0, 0, 0)), v, 1e-15, "each token sees only itself")
+
+
+def pin_window_1d_band(impl):
+    """On a 1 x 1 x N grid the window is a band |i - j| <= r in token order:
+    plain attention of each row on the rotated keys of its band."""
+    g1, r = (1, 1, N), 3
+    q, k, v = _data(22)
+    got = impl.window(q, k, v, g1, SPLIT, THETA, SCALE, (0, 0, r))
+    pos = reference.grid_positions(g1)
+    qr, kr = reference.rope3d_at(q, pos, SPLIT, THETA), reference.rope3d_at(k, pos, SPLIT, THETA)
+    for i in range(N):
+        lo, hi = max(0, i - r), min(N, i + r + 1)
+        _close(got[i:i + 1], reference.attention(qr[i:i + 1], kr[lo:hi], v[lo:hi], SCALE), 1e-14, f"band row {i}")
+
+
+def pin_window_brute(impl):
+    q, k, v = _data(23)
+    radius = (0, 1, 2)  # unequal per axis, to catch a swapped axis
+    _close(impl.window(q, k, v, GRID, SPLIT, THETA, SCALE, radius),
+           brute.window_attend(q.tolist(), k.tolist(), v.tolist(), GRID, SPLIT, THETA, SCALE, radius), 1e-12,
+           "window vs brute force")
+
+
+def test_window_visibility_is_symmetric_and_contains_self():
+    vis = reference.window_visible((3, 4, 5), (1, 0, 2))
+    assert np.array_equal(vis, vis.T) and np.all(np.diag(vis))
+
+
+WPINS = [pin_window_large_radius_is_dense, pin_window_zero_radius_is_identity_on_v, pin_window_1d_band,
+         pin_window_brute]
+
+
+@pytest.mark.parametrize("pin", WPINS, ids=lambda p: p.__name__)
+def test_window_pin(pin):
+    pin(WIMPL)
+
+
+def _window_with(vis_fn):
+    def impl(q, k, v, grid, split, theta, scale, radius, rows=None, rope=True):
+        pos = reference.grid_positions(grid)
+        qr, kr = reference.rope3d_at(q, pos, split, theta), reference.rope3d_at(k, pos, split, theta)
+        vis = vis_fn(pos, np.asarray(radius))
+        out = np.zeros((len(qr), np.asarray(v).shape[1]))
+        for i in range(len(qr)):
+            if not vis[i].any():
+                raise ValueError("no visible key")
+            s = scale * (kr[vis[i]] @ qr[i])
+            e = np.exp(s - s.max())
+            out[i] = (e / e.sum()) @ np.asarray(v)[vis[i]]
+        return out
+    return impl
+
+
+WMUTANTS = {
+    "strict inequality": _window_with(lambda p, r: np.all(np.abs(p[:, None] - p[None]) < r, axis=2)),
+    "radius axes reversed": _window_with(lambda p, r: np.all(np.abs(p[:, None] - p[None]) <= r[::-1], axis=2)),
+    "window anchored at the query, not centred": _window_with(
+        lambda p, r: np.all((p[None] - p[:, None] >= 0) & (p[None] - p[:, None] <= r), axis=2)),
+    "radius on the flat token index": _window_with(
+        lambda p, r: np.abs(np.arange(len(p))[:, None] - np.arange(len(p))[None]) <= r.sum()),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WMUTANTS))
+def test_window_pins_catch(name):
+    caught = []
+    for pin in WPINS:
+        try:
+            pin(types.SimpleNamespace(window=WMUTANTS[name]))
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches: {name}"
+
+
+def test_window_harness_without_mistake_is_the_oracle():
+    q, k, v = _data(24)
+    exact = _window_with(lambda p, r: np.all(np.abs(p[:, None] - p[None]) <= r, axis=2))
+    _close(exact(q, k, v, GRID, SPLIT, THETA, SCALE, (1, 1, 2)),
+           reference.window_attention(q, k, v, GRID, SPLIT, THETA, SCALE, (1, 1, 2)), 1e-14, "harness")
