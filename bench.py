@@ -104,9 +104,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="host time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--variant", choices=("dense", "subset", "sparse"), default="dense",
+    ap.add_argument("--variant", choices=("dense", "subset", "sparse", "window"), default="dense",
                     help="subset: a quarter of the query tokens attend to all keys; sparse: block-sparse lists "
-                         "(a band of 96 key blocks each side of the query block plus 96 global key blocks)")
+                         "(a band of 96 key blocks each side of the query block plus 96 global key blocks); "
+                         "window: local window of radius (1, 7, 7) around each query")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the timed region, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling memory counters)")
@@ -235,6 +236,8 @@ def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
     import workloads as wlmod
 
     QB, KB = va.SPARSE_Q_BLOCK, va.SPARSE_K_BLOCK
+    if args.variant == "window":
+        return window_bench(args, va, wl, host, q, k, v, rope, stream)
     if args.variant == "subset":
         idx = wlmod.subset_index(wl, wl.N // 4)
         q_sub = torch.from_numpy(np.ascontiguousarray(host["q"][:, :, idx]).view(np.int16)).cuda().view(torch.bfloat16)
@@ -303,6 +306,90 @@ def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
                     ref = oracle.block_sparse_attention(dec(host["q"][b, h]), dec(host["k"][b, h]),
                                                         dec(host["v"][b, h]), wl.grid, wl.split, wl.theta, wl.scale,
                                                         blocks[b, h], count[b, h], QB, KB, rows=rows)
+            got = oracle.decode_bf16(o[b, h, torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy()
+                                     .view(np.uint16))
+            e = np.abs(got - ref)
+            worst["max_abs"] = max(worst["max_abs"], float(e.max()))
+            worst["mean_rel"] = max(worst["mean_rel"], float(e.sum() / np.abs(ref).sum()))
+        result["parity_sample"] = {**{k2: round(v2, 7) for k2, v2 in worst.items()},
+                                   "slices": "(0,0) and (B-1,heads-1), 256 rows each"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def window_tiles(wl, radius):
+    """Query-key pairs the window attention visits (the 64-key tiles its plan
+    lists per 256-query block, times the block's rows) and the pairs inside
+    the windows; mirrors the planning rule (whole rows of every frame in
+    range)."""
+    F, H, W = wl.grid
+    hw, N = H * W, wl.N
+    rf, rh, rw = radius
+    visited = 0
+    for i in range(-(-N // 256)):
+        q0, q1 = 256 * i, min(N, 256 * i + 256) - 1
+        fa, fb = q0 // hw, q1 // hw
+        ya, yb = ((q0 - fa * hw) // W, (q1 - fb * hw) // W) if fa == fb else (0, H - 1)
+        f0, f1, y0, y1 = max(0, fa - rf), min(F - 1, fb + rf), max(0, ya - rh), min(H - 1, yb + rh)
+        tiles, last = 0, -1
+        for f in range(f0, f1 + 1):
+            t0, t1 = ((f * H + y0) * W) // 64, ((f * H + y1) * W + W - 1) // 64
+            tiles += max(0, t1 - max(t0, last + 1) + 1)
+            last = max(last, t1)
+        visited += tiles * 64 * (q1 - q0 + 1)
+    ext = lambda n, r: sum(min(n - 1, c + r) - max(0, c - r) + 1 for c in range(n))
+    inside = ext(F, rf) * ext(H, rh) * ext(W, rw)
+    return visited, inside
+
+
+def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
+    """Local-window attention of radius (1, 7, 7): a call is pre-pass + plan
+    + attention; FLOPs count the query-key pairs of the visited tiles (the
+    roofline) and, apart, the pairs inside the windows."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wlmod
+
+    radius = (1, 7, 7)
+    visited, inside = window_tiles(wl, radius)
+    flops = 4.0 * wl.B * wl.heads * visited * wl.d
+    n = va.vidattn_fwd_window_workspace_size(va.BF16, wl.B, wl.heads, wl.N, wl.d, True)
+    wws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    call = lambda: va.window_attention(q, k, v, radius, grid=wl.grid, split=wl.split, theta=wl.theta,
+                                       scale=wl.scale, workspace=wws, out=o, stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in es:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = statistics.mean(a.elapsed_time(b) for a, b in es)
+    result = {
+        "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {**wl.describe(), "workload": f"{wl.name}-window-r{radius[0]}{radius[1]}{radius[2]}",
+                   "variant": "window", "radius": list(radius), "flops_per_call": flops,
+                   "visited_fraction": round(visited / wl.N ** 2, 4),
+                   "pairs_inside_windows_fraction": round(inside / wl.N ** 2, 5)},
+        "roofline": {"kernel": KERNEL, "bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+                     "traffic": None, "note": "whole call (pre-pass + plan + attention) against visited-tile FLOPs"},
+    }
+    if not args.no_parity:
+        from threadpoolctl import threadpool_limits
+        worst = dict(max_abs=0.0, mean_rel=0.0)
+        for (b, h) in [(0, 0), (wl.B - 1, wl.heads - 1)]:
+            rows = wlmod.sample_rows(wl, b, h)
+            with threadpool_limits(16):
+                ref = oracle.window_attention(*(oracle.decode_bf16(host[t][b, h]) for t in ("q", "k", "v")),
+                                              wl.grid, wl.split, wl.theta, wl.scale, radius, rows=rows)
             got = oracle.decode_bf16(o[b, h, torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy()
                                      .view(np.uint16))
             e = np.abs(got - ref)

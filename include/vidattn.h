@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define VIDATTN_ABI_VERSION 2
+#define VIDATTN_ABI_VERSION 3
 
 typedef enum {
   VIDATTN_OK = 0,
@@ -219,6 +219,42 @@ vidattn_status vidattn_fwd_attend_block_sparse(const void* q, const void* worksp
                                                const vidattn_rope3d_desc* rope, const int32_t* kv_blocks,
                                                const int32_t* kv_count, int64_t max_blocks, size_t workspace_bytes,
                                                void* hip_stream);
+
+/* Local window over the token grid: a query at grid position (f, y, x)
+ * attends to the keys (f', y', x') with |f - f'| <= r_f, |y - y'| <= r_h and
+ * |x - x'| <= r_w (a centred box, clipped at the grid border; every query
+ * sees at least itself). F, H, W as in vidattn_rope3d_desc (F*H*W == N);
+ * radii >= 0, and a radius at or beyond its extent reaches the whole axis. */
+typedef struct {
+  int64_t F, H, W;
+  int32_t r_f, r_h, r_w;
+} vidattn_window_desc;
+
+/* Local-window attention: vidattn_fwd with every query restricted to its
+ * window, the windowed-attention primitive of the vidax summary
+ * (paperlayer.ai/abs/2609.18077v1, "2 System Architecture & Design", heading
+ * "3D RoPE, 3D VAEs, and flash attention") and the sliding local windows of
+ * Sparse Forcing (its abstract on thelatestinai.com/papers/2606.17566); the
+ * pages fix no window shape, the centred box above is the plainest reading.
+ * One call runs the key/value pre-pass, a planning kernel that lists per
+ * 256-query block the 64-key tiles meeting its queries' windows (in the
+ * workspace), and the attention over those tiles with the keys outside each
+ * query's box masked. Arguments as for vidattn_fwd, plus:
+ *   window     non-null; its grid must equal rope's when rope is given.
+ *   workspace  at least vidattn_fwd_window_workspace_size(...) bytes.
+ * An unbounded window gives the vidattn_fwd result bit for bit. Only BF16 is
+ * implemented (F32: UNSUPPORTED). */
+vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,
+                                  int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                                  const vidattn_rope3d_desc* rope, const vidattn_window_desc* window,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes vidattn_fwd_window needs: vidattn_fwd_workspace_size plus
+ * the tile lists, 4*(ceil(N/256)*ceil(N/64)) bytes and a 256-byte-padded
+ * count array. 0 for arguments vidattn_fwd_window would reject by dtype or
+ * size. */
+size_t vidattn_fwd_window_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                         int use_rope);
 
 /* Workspace bytes vidattn_fwd needs for these sizes (0 if none). Returns 0
  * also for arguments vidattn_fwd would reject; a positive size never

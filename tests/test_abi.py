@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_strings():
-    assert va.vidattn_abi_version() == 2
+    assert va.vidattn_abi_version() == 3
     for s, txt in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "workspace too small"),
                    (4, "HIP error")]:
         assert va.vidattn_status_string(s) == txt
@@ -182,6 +182,26 @@ def test_attend_block_sparse_rejects():
     assert bs(workspace_bytes=wsb - 1) == 3
     assert bs(d=96) == 2
     assert bs(o=QF) == 1 and "overlaps q" in va.vidattn_last_error()
+
+
+def test_window_rejects_and_sizes():
+    base = va.vidattn_fwd_workspace_size(va.BF16, 2, 40, N5, 128, 1)
+    wsb = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1)
+    nqb, nkt = -(-N5 // 256), -(-N5 // 64)
+    assert wsb == base + (nqb * 4 + 255) // 256 * 256 + nqb * nkt * 4
+    assert va.vidattn_fwd_window_workspace_size(va.F32, 2, 40, N5, 128, 1) == 0
+    W = va.WindowDesc.make((21, 45, 80), (1, 4, 4))
+    win = lambda **kw: va.vidattn_fwd_window(**{**dict(
+        q=QF, k=QF + T // 4, v=QF + T // 2, o=OF, dt=va.BF16, B=2, heads=40, N=N5, d=128, softmax_scale=0.1,
+        rope=GOOD, window=W, workspace=WSF, workspace_bytes=wsb), **kw})
+    assert win(dt=va.F32) == 2
+    assert win(window=None) == 1 and "window" in va.vidattn_last_error()
+    assert win(window=va.WindowDesc.make((21, 45, 81), (1, 1, 1))) == 1 and "N" in va.vidattn_last_error()
+    assert win(window=va.WindowDesc.make((21, 45, 80), (-1, 1, 1))) == 1 and "radii" in va.vidattn_last_error()
+    assert win(rope=Rope3dDesc.make((21, 80, 45), (44, 42, 42), 1e4)) == 1 and "grids differ" in va.vidattn_last_error()
+    assert win(workspace_bytes=wsb - 1) == 3
+    assert win(workspace_bytes=base) == 3
+    assert win(softmax_scale=0.0) == 1
 
 
 def test_single_hip_runtime_whatever_the_import_order():

@@ -1,4 +1,4 @@
-"""Parity of the query-subset and block-sparse attention (HIP path through
+"""Parity of the query-subset, block-sparse and local-window attention (HIP path through
 the C ABI) with the fp64 CPU oracle on the same seeded inputs, plus the
 identities that tie them to the dense attention. Needs an MI355X."""
 import numpy as np
@@ -263,5 +263,68 @@ def test_sparse_large(va):
     rows = wlmod.sample_rows(wl, 0, 0)
     _log(f"sparse {wl.name} window=16 global=32 max={blocks.shape[-1]}")
     _, st = _check_sparse(va, wl, host, blocks, count, rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)])
+    _log(f"  {st}")
+    assert _within(st), st
+
+
+# ------------------------------------------------------------------ local window
+
+WINDOW_CASES = [
+    # grid, d, split, B, H, radius (frame, row, column)
+    ((3, 11, 17), 128, (44, 42, 42), 2, 2, (1, 2, 3)),
+    ((3, 11, 17), 64, (16, 24, 24), 1, 3, (0, 1, 1)),
+    ((5, 13, 17), 128, (44, 42, 42), 1, 2, (2, 0, 5)),
+    ((2, 9, 11), 128, (44, 42, 42), 2, 1, (0, 0, 0)),
+    ((6, 5, 7), 128, (44, 42, 42), 1, 2, (1, 4, 2)),
+    ((4, 8, 8), 64, (16, 24, 24), 1, 1, (3, 1, 0)),
+]
+
+
+def _check_window(va, wl, host, radius, rope=True, rows=None, slices=None):
+    q, k, v = (parity.to_torch(host[n]) for n in ("q", "k", "v"))
+    o = va.window_attention(q, k, v, radius, grid=wl.grid, split=wl.split, theta=wl.theta, scale=wl.scale, rope=rope)
+    torch.cuda.synchronize()
+    parts = []
+    for (b, h) in (slices or [(b, h) for b in range(wl.B) for h in range(wl.heads)]):
+        r = np.arange(wl.N) if rows is None else rows
+        got = parity.from_torch(o[b, h, torch.from_numpy(r).cuda()])
+        qd, kd, vd = (parity.decode(wl, host[n][b, h]) for n in ("q", "k", "v"))
+        ref = oracle.window_attention(qd, kd, vd, wl.grid, wl.split, wl.theta, wl.scale, radius, rows=r, rope=rope)
+        parts.append(_stats(got, ref))
+    return o, _merge(parts)
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES,
+                         ids=lambda c: f"{c[0][0]}x{c[0][1]}x{c[0][2]}-d{c[1]}-r{c[5][0]}{c[5][1]}{c[5][2]}")
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
+def test_window_small(va, case, rope):
+    grid, d, split, B, H, radius = case
+    wl = wlmod.custom(B, H, grid, d, split, seed_id=680 + d + sum(radius))
+    host = parity.host_inputs(wl)
+    _log(f"window {wl.name} radius={radius} rope={rope}")
+    _, st = _check_window(va, wl, host, radius, rope)
+    _log(f"  {st}")
+    assert _within(st), st
+
+
+def test_window_unbounded_is_the_dense_attention_bitwise(va):
+    wl = wlmod.custom(2, 2, (3, 11, 17), 128, (44, 42, 42), seed_id=690)
+    host = parity.host_inputs(wl)
+    q, k, v = (parity.to_torch(host[n]) for n in ("q", "k", "v"))
+    kw = dict(grid=wl.grid, split=wl.split, theta=wl.theta, scale=wl.scale)
+    a = va.window_attention(q, k, v, (1 << 30, 1 << 30, 1 << 30), **kw)
+    b = va.attention(q, k, v, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_window_large(va):
+    """The 32760-token grid (21 x 30 x 52) with radius (2, 6, 6); 256 sampled
+    rows of two slices."""
+    wl = wlmod.WORKLOADS[2]
+    host = parity.host_inputs(wl)
+    rows = wlmod.sample_rows(wl, 0, 0)
+    _log(f"window {wl.name} radius=(2, 6, 6)")
+    _, st = _check_window(va, wl, host, (2, 6, 6), rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)])
     _log(f"  {st}")
     assert _within(st), st

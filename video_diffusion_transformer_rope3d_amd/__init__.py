@@ -19,17 +19,18 @@ __all__ = [
     "vidattn_fwd_attend_block_sparse", "vidattn_fwd_workspace_size", "vidattn_status_string",
     "vidattn_last_error", "vidattn_abi_version", "attention", "prepare", "attend", "attend_subset",
     "attend_block_sparse", "rope3d", "workspace_for", "SPARSE_Q_BLOCK", "SPARSE_K_BLOCK", "EXPORTED_SYMBOLS",
+    "WindowDesc", "vidattn_fwd_window", "vidattn_fwd_window_workspace_size", "window_attention",
 ]
 
 BF16, F16, F32 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 SPARSE_Q_BLOCK, SPARSE_K_BLOCK = 256, 64  # VIDATTN_SPARSE_Q_BLOCK, VIDATTN_SPARSE_K_BLOCK
 
 EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend",
-                    "vidattn_fwd_attend_subset", "vidattn_fwd_attend_block_sparse",
-                    "vidattn_fwd_workspace_size", "vidattn_status_string", "vidattn_last_error",
+                    "vidattn_fwd_attend_subset", "vidattn_fwd_attend_block_sparse", "vidattn_fwd_window",
+                    "vidattn_fwd_window_workspace_size", "vidattn_fwd_workspace_size", "vidattn_status_string", "vidattn_last_error",
                     "vidattn_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +57,19 @@ class Rope3dDesc(ctypes.Structure):
         F, H, W = (int(g) for g in grid)
         d_t, d_h, d_w = (int(s) for s in split)
         return cls(F, H, W, d_t, d_h, d_w, float(theta))
+
+
+class WindowDesc(ctypes.Structure):
+    """vidattn_window_desc: the token grid and the window radii (frame, row,
+    column)."""
+    _fields_ = [("F", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
+                ("r_f", ctypes.c_int32), ("r_h", ctypes.c_int32), ("r_w", ctypes.c_int32)]
+
+    @classmethod
+    def make(cls, grid, radius) -> "WindowDesc":
+        F, H, W = (int(g) for g in grid)
+        r_f, r_h, r_w = (int(r) for r in radius)
+        return cls(F, H, W, r_f, r_h, r_w)
 
 
 _LIB = None
@@ -116,6 +130,11 @@ def load() -> ctypes.CDLL:
     lib.vidattn_fwd_attend_block_sparse.restype = ctypes.c_int
     lib.vidattn_fwd_attend_block_sparse.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                                     ctypes.POINTER(Rope3dDesc), vp, vp, i64, sz, vp]
+    lib.vidattn_fwd_window.restype = ctypes.c_int
+    lib.vidattn_fwd_window.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
+                                       ctypes.POINTER(Rope3dDesc), ctypes.POINTER(WindowDesc), vp, sz, vp]
+    lib.vidattn_fwd_window_workspace_size.restype = sz
+    lib.vidattn_fwd_window_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
     lib.vidattn_fwd_workspace_size.restype = sz
     lib.vidattn_fwd_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
     lib.vidattn_status_string.restype = ctypes.c_char_p
@@ -171,6 +190,18 @@ def vidattn_fwd_attend_block_sparse(q, workspace, o, dt, B, heads, N, d, softmax
     return load().vidattn_fwd_attend_block_sparse(q, workspace, o, dt, B, heads, N, d, softmax_scale,
                                                   ctypes.byref(rope) if rope is not None else None, kv_blocks,
                                                   kv_count, max_blocks, workspace_bytes, stream)
+
+
+def vidattn_fwd_window(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, window, workspace, workspace_bytes,
+                       stream=None) -> int:
+    return load().vidattn_fwd_window(q, k, v, o, dt, B, heads, N, d, softmax_scale,
+                                     ctypes.byref(rope) if rope is not None else None,
+                                     ctypes.byref(window) if window is not None else None, workspace,
+                                     workspace_bytes, stream)
+
+
+def vidattn_fwd_window_workspace_size(dt, B, heads, N, d, use_rope) -> int:
+    return load().vidattn_fwd_window_workspace_size(dt, B, heads, N, d, int(bool(use_rope)))
 
 
 def vidattn_fwd_workspace_size(dt, B, heads, N, d, use_rope) -> int:
@@ -330,6 +361,28 @@ def attend_block_sparse(q, workspace, kv_blocks, kv_count, *, scale=None, grid=N
     _raise(vidattn_fwd_attend_block_sparse(q.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s, rope,
                                            kv_blocks.data_ptr(), kv_count.data_ptr(), kv_blocks.shape[3], nbytes,
                                            _stream(stream)))
+    return out
+
+
+def window_attention(q, k, v, radius, *, grid, split=None, theta=10000.0, scale=None, rope=True, workspace=None,
+                     out=None, stream=None):
+    """Local-window attention (BF16): each query attends to the keys within
+    ``radius`` = (r_f, r_h, r_w) of its position on the token ``grid``
+    (rotary embedding on ``grid`` with ``split`` unless rope=False)."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    rd = Rope3dDesc.make(grid, split, theta) if rope else None
+    wd = WindowDesc.make(grid, radius)
+    if workspace is None:
+        n = vidattn_fwd_window_workspace_size(_dt(q), B, H, N, d, rope)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    ptr, nbytes = _ws(workspace)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _raise(vidattn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(q), B, H, N, d, s, rd, wd,
+                              ptr, nbytes, _stream(stream)))
     return out
 
 

@@ -30,14 +30,19 @@
 // when a tile's probability sum exceeds 2^20 (then the tile is redone against
 // the exact maximum and O, l are scaled).
 //
-// Two variants share the loop. Query subset: Nq query rows (Nq may differ
+// Three variants share the loop. Query subset: Nq query rows (Nq may differ
 // from the Nk keys) whose rotary positions are the token indices qidx[row]
 // (qidx == nullptr: row r is token r). Block-sparse (SPARSE): each
 // (b, head, 256-query block) visits only the 64-key tiles listed in
 // kvb[.][0 .. kvc[.]-1] (ascending), so "tile j" of the loop is the j-th
-// listed tile; a block with no listed tile gets O = 0. Indices read from
-// device memory are clamped into range, so no input can address outside the
-// workspace.
+// listed tile; a block with no listed tile gets O = 0; the lists may be
+// shared by every (b, head) (lists_shared). Local window (WIN, on top of
+// SPARSE): in the listed tiles, keys outside the box of radii (r_f, r_h,
+// r_w) around the query's grid position get -inf. Indices read from device
+// memory are clamped into range, so no input can address outside the
+// workspace. The exact step runs for a row until the row has seen a visible
+// key (in the dense case: on the first tile), so tiles whose keys are all
+// masked for some rows leave m untouched.
 #pragma once
 
 #include <type_traits>
@@ -52,11 +57,19 @@
 
 namespace vidattn {
 
-template <int D, int NS, bool SPARSE>
+// Box of a local window over the F x H x W token grid.
+struct WindowParams {
+  int F, H, W;
+  int rf, rh, rw;
+};
+
+template <int D, int NS, bool SPARSE, bool WIN = false>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ ws, uint16_t* __restrict__ O, int N, int nkt, int Nq,
     int ntq, int total_wg, float qscale, RopeParams rp, const int32_t* __restrict__ qidx,
-    const int32_t* __restrict__ kvb, const int32_t* __restrict__ kvc, int maxb) {
+    const int32_t* __restrict__ kvb, const int32_t* __restrict__ kvc, int maxb, int lists_shared,
+    WindowParams wp) {
+  static_assert(SPARSE || !WIN, "the window visits listed tiles");
   constexpr int NW = 8;
   constexpr int KT = 64;
   constexpr int BR = NW * 32;
@@ -90,10 +103,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
 
   // Key tiles this workgroup visits: all nkt (dense) or its list (SPARSE).
   // Loop position j maps to workspace tile tile_at(j), clamped into range.
-  const int32_t* lst = SPARSE ? kvb + ((int64_t)bh * ntq + qt) * maxb : nullptr;
+  const int64_t lrow = lists_shared ? (int64_t)qt : (int64_t)bh * ntq + qt;
+  const int32_t* lst = SPARSE ? kvb + lrow * maxb : nullptr;
   int nt = nkt;
   if constexpr (SPARSE) {
-    const int c = kvc[(int64_t)bh * ntq + qt];
+    const int c = kvc[lrow];
     nt = c < 0 ? 0 : (c > maxb ? maxb : c);
   }
   auto tile_at = [&](int j) __attribute__((always_inline)) {
@@ -174,6 +188,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   f32x16 sacc[2];
   bf16x8 pk[MS];
   float m = 0.f, l = 0.f;
+  bool m_valid = false;  // this row's m comes from a visible key
+  // grid position of this lane's query (window variant)
+  int qf = 0, qy = 0, qx = 0;
+  if constexpr (WIN) {
+    const int qrow = qt * BR + wave * 32 + qi;
+    const int t = qrow < N ? qrow : N - 1;
+    const int hw = wp.H * wp.W;
+    qf = t / hw;
+    qy = (t - qf * hw) / wp.W;
+    qx = t - qf * hw - qy * wp.W;
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) negm[i] = 0.f;
 #pragma unroll
@@ -292,17 +317,50 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           }
       }
     }
+    if constexpr (WIN) {
+      // keys outside the query's window (and past N) get -inf. Lane keys come
+      // in runs of 8 consecutive tokens starting at 32kb + 16h + 8g; each run
+      // decodes its first key and steps along the column index.
+      const int base = tile_at(jj) * KT;
+      const int hw = wp.H * wp.W;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k0 = base + 32 * kb + 16 * h + 8 * g;
+          int f = k0 / hw;
+          int y = (k0 - f * hw) / wp.W;
+          int x = k0 - f * hw - y * wp.W;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool vis = k0 + e < N && abs(f - qf) <= wp.rf && abs(y - qy) <= wp.rh && abs(x - qx) <= wp.rw;
+            if (!vis) sacc[kb][8 * h + e] = -INFINITY;
+            // next token: column + 1, carrying into row and frame
+            ++x;
+            const bool cx = x >= wp.W;
+            x = cx ? 0 : x;
+            y += cx ? 1 : 0;
+            const bool cy = y >= wp.H;
+            y = cy ? 0 : y;
+            f += cy ? 1 : 0;
+          }
+        }
+    }
     float ls = probs();
-    if (__builtin_amdgcn_ballot_w64(jj == 0 || !(ls <= kRescaleSum)) != 0) {
-      // exact maximum of the tile (relative to the current m)
+    if (__builtin_amdgcn_ballot_w64(!m_valid || !(ls <= kRescaleSum)) != 0) {
+      // exact maximum of the tile (relative to the current m); a row that
+      // has seen no visible key yet takes the tile's maximum as its m (and
+      // keeps m = 0 if the tile shows it none)
       float mx = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
       mx = xor32_max(mx);
-      const float delta = jj == 0 ? mx : fmaxf(mx, 0.f);
-      const float alpha = jj == 0 ? 1.f : __builtin_amdgcn_exp2f(-delta);
+      const bool seen = mx > -INFINITY;
+      const float delta = !m_valid ? (seen ? mx : 0.f) : fmaxf(mx, 0.f);
+      const float alpha = !m_valid ? 1.f : __builtin_amdgcn_exp2f(-delta);
+      m_valid = m_valid || seen;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)

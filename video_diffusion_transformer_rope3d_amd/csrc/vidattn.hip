@@ -1,6 +1,7 @@
 // libvidattn: C ABI entry points (declared and documented in include/vidattn.h).
 // Host side: argument validation (before any HIP call), rotary parameter
 // setup, workspace sizing and kernel launches on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -11,6 +12,7 @@
 #include "attn_bf16_pp.hpp"
 #include "attn_f32.hpp"
 #include "rope_kernels.hpp"
+#include "window_plan.hpp"
 
 using namespace vidattn;
 
@@ -216,7 +218,7 @@ enum class Phase { kFused, kPrepare, kAttend };
 vidattn_status validate_fwd(Phase ph, const void* q, const void* k, const void* v, const void* o, vidattn_dtype dt,
                             int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
                             const vidattn_rope3d_desc* rope, const void* workspace, size_t workspace_bytes,
-                            int64_t Nq = -1) {
+                            int64_t Nq = -1, size_t extra_workspace = 0) {
   if (Nq < 0) Nq = N;  // rows of q and o (a query subset may have fewer or more than the N keys)
   if (!q || !k || !v || !o) return fail(VIDATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -240,7 +242,7 @@ vidattn_status validate_fwd(Phase ph, const void* q, const void* k, const void* 
     return fail(VIDATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (rope)
     if (vidattn_status s = check_rope(rope, d, N, true)) return s;
-  const size_t need = vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
+  const size_t need = vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr) + extra_workspace;
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(VIDATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need,
@@ -310,17 +312,20 @@ vidattn_status launch_prepare(const void* k, const void* v, vidattn_dtype dt, in
 struct AttendExtras {
   int64_t Nq = -1;  // -1: Nq = N
   const int32_t* qidx = nullptr;
-  const int32_t* kvb = nullptr;
+  const int32_t* kvb = nullptr;  // non-null: block-sparse lists
   const int32_t* kvc = nullptr;
   int maxb = 0;
+  int lists_shared = 0;  // one list per query block for every (b, head)
+  bool window = false;   // mask keys outside each query's box
+  WindowParams wp{1, 1, 1, 0, 0, 0};
 };
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool WIN>
 void launch_bf16(const void* q, const uint8_t* ws, void* o, int N, int nkt, int Nq, int ntq, int total, float qscale,
                  const RopeParams& rp, const AttendExtras& x, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<D, VIDATTN_BF16_NS, SPARSE>), dim3((unsigned)total), dim3(kNW * 64), 0,
-                     st, static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), N, nkt, Nq, ntq, total,
-                     qscale, rp, x.qidx, x.kvb, x.kvc, x.maxb);
+  hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<D, VIDATTN_BF16_NS, SPARSE, WIN>), dim3((unsigned)total),
+                     dim3(kNW * 64), 0, st, static_cast<const uint16_t*>(q), ws, static_cast<uint16_t*>(o), N, nkt,
+                     Nq, ntq, total, qscale, rp, x.qidx, x.kvb, x.kvc, x.maxb, x.lists_shared, x.wp);
 }
 
 vidattn_status launch_attend(const void* q, const void* k, const void* v, const void* workspace, void* o,
@@ -335,16 +340,21 @@ vidattn_status launch_attend(const void* q, const void* k, const void* v, const 
     const int total = (int)(nbh * ntq);
     const uint8_t* ws = static_cast<const uint8_t*>(workspace);
     const bool sparse = x.kvb != nullptr;
+    const int n = (int)N, nq = (int)Nq;
     if (d == 128) {
-      if (sparse)
-        launch_bf16<128, true>(q, ws, o, (int)N, nkt, (int)Nq, ntq, total, qscale, rp, x, st);
+      if (x.window)
+        launch_bf16<128, true, true>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+      else if (sparse)
+        launch_bf16<128, true, false>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
       else
-        launch_bf16<128, false>(q, ws, o, (int)N, nkt, (int)Nq, ntq, total, qscale, rp, x, st);
+        launch_bf16<128, false, false>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
     } else {
-      if (sparse)
-        launch_bf16<64, true>(q, ws, o, (int)N, nkt, (int)Nq, ntq, total, qscale, rp, x, st);
+      if (x.window)
+        launch_bf16<64, true, true>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+      else if (sparse)
+        launch_bf16<64, true, false>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
       else
-        launch_bf16<64, false>(q, ws, o, (int)N, nkt, (int)Nq, ntq, total, qscale, rp, x, st);
+        launch_bf16<64, false, false>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
     }
     return hip_check("bf16 attention launch");
   }
@@ -453,6 +463,73 @@ vidattn_status vidattn_fwd_attend_block_sparse(const void* q, const void* worksp
   if (vidattn_status s = launch_attend(q, q, q, workspace, o, dt, B * heads, N, d, softmax_scale, rp,
                                        static_cast<hipStream_t>(hip_stream), x))
     return s;
+  return ok();
+}
+
+
+// Workspace of the local-window attention: the key/value image, then the
+// per-query-block tile counts (padded to 256 bytes), then the tile lists
+// (ceil(N/256) rows of ceil(N/64) entries).
+static size_t window_plan_bytes(int64_t N) {
+  const int64_t nqb = (N + kBR - 1) / kBR, nkt = (N + kKT - 1) / kKT;
+  return (size_t)((nqb * 4 + 255) / 256 * 256 + nqb * nkt * 4);
+}
+
+static vidattn_status check_window(const vidattn_window_desc* w, int64_t N, const vidattn_rope3d_desc* rope) {
+  if (!w) return fail(VIDATTN_ERR_INVALID_ARG, "window must be non-null");
+  if (w->F < 1 || w->H < 1 || w->W < 1) return fail(VIDATTN_ERR_INVALID_ARG, "window grid extents must be >= 1");
+  int64_t hw, fhw;
+  if (!mul_ok(w->H, w->W, &hw) || !mul_ok(w->F, hw, &fhw) || fhw != N)
+    return fail(VIDATTN_ERR_INVALID_ARG, "window grid F*H*W does not equal N = %lld", (long long)N);
+  if (w->r_f < 0 || w->r_h < 0 || w->r_w < 0) return fail(VIDATTN_ERR_INVALID_ARG, "window radii must be >= 0");
+  if (rope && (rope->F != w->F || rope->H != w->H || rope->W != w->W))
+    return fail(VIDATTN_ERR_INVALID_ARG, "window and rotary grids differ");
+  return VIDATTN_OK;
+}
+
+size_t vidattn_fwd_window_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                         int use_rope) {
+  if (dt != VIDATTN_BF16) return 0;
+  const size_t base = vidattn_fwd_workspace_size(dt, B, heads, N, d, use_rope);
+  return base ? base + window_plan_bytes(N) : 0;
+}
+
+vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,
+                                  int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                                  const vidattn_rope3d_desc* rope, const vidattn_window_desc* window,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (dt != VIDATTN_BF16)
+    return fail(dt == VIDATTN_F32 || dt == VIDATTN_F16 ? VIDATTN_ERR_UNSUPPORTED : VIDATTN_ERR_INVALID_ARG,
+                "local-window attention is implemented for BF16");
+  if (N >= 1 && N <= kMaxN)
+    if (vidattn_status s = check_window(window, N, rope)) return s;
+  const size_t plan = N >= 1 && N <= kMaxN ? window_plan_bytes(N) : 0;
+  if (vidattn_status s = validate_fwd(Phase::kFused, q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, workspace,
+                                      workspace_bytes, -1, plan))
+    return s;
+  if (!window) return fail(VIDATTN_ERR_INVALID_ARG, "window must be non-null");
+  const RopeParams rp = make_rope(rope);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (vidattn_status s = launch_prepare(k, v, dt, B * heads, N, d, rp, workspace, st)) return s;
+  const int64_t nqb = (N + kBR - 1) / kBR, nkt = (N + kKT - 1) / kKT;
+  uint8_t* tail = static_cast<uint8_t*>(workspace) + vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
+  int32_t* kvc = reinterpret_cast<int32_t*>(tail);
+  int32_t* kvb = reinterpret_cast<int32_t*>(tail + (nqb * 4 + 255) / 256 * 256);
+  hipLaunchKernelGGL(window_plan_kernel, dim3((unsigned)((nqb + 255) / 256)), dim3(256), 0, st, kvb, kvc, (int)N,
+                     (int)nqb, (int)nkt, (int)window->F, (int)window->H, (int)window->W,
+                     (int)std::min<int64_t>(window->r_f, window->F), (int)std::min<int64_t>(window->r_h, window->H));
+  if (vidattn_status s = hip_check("window plan launch")) return s;
+  AttendExtras x;
+  x.kvb = kvb;
+  x.kvc = kvc;
+  x.maxb = (int)nkt;
+  x.lists_shared = 1;
+  x.window = true;
+  // a radius at or beyond the grid extent reaches the whole axis
+  const int rf = (int)std::min<int64_t>(window->r_f, window->F), rh = (int)std::min<int64_t>(window->r_h, window->H),
+            rw = (int)std::min<int64_t>(window->r_w, window->W);
+  x.wp = WindowParams{(int)window->F, (int)window->H, (int)window->W, rf, rh, rw};
+  if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, B * heads, N, d, softmax_scale, rp, st, x)) return s;
   return ok();
 }
 
