@@ -57,10 +57,16 @@
 
 namespace vidattn {
 
-// Box of a local window over the F x H x W token grid.
+// Box of a local window over the F x H x W token grid. With fast != 0 (the
+// host sets it when W >= 8 and every key index is below 2^22) a key index k
+// is split into row k / W and column k % W as (int)fma(k, invW, invW / 2):
+// the exact quotient plus (r + 1/2) / W lies at least 1/(2W) from an integer
+// and the fp32 error stays below that for k < 2^22 (the same for row / H).
 struct WindowParams {
   int F, H, W;
   int rf, rh, rw;
+  int fast;
+  float invW, invH;
 };
 
 template <int D, int NS, bool SPARSE, bool WIN = false>
@@ -189,15 +195,26 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   bf16x8 pk[MS];
   float m = 0.f, l = 0.f;
   bool m_valid = false;  // this row's m comes from a visible key
-  // grid position of this lane's query (window variant)
-  int qf = 0, qy = 0, qx = 0;
+  // Window of this lane's query (window variant): a key at (f, y, x) is
+  // visible when f - flo, y - ylo and x - clo, as unsigned, are at most
+  // 2 r_f, 2 r_h and 2 r_w. For the fast test, a run of 8 keys starting at
+  // column c0 of row r0 sees columns [clo, cend) of row r0 and, after the
+  // row wrap, [wlo, wend) counted from the run's start as W - c0 + column.
+  int flo = 0, ylo = 0, clo = 0, cend = 0, wlo = 0, wend = 0;
   if constexpr (WIN) {
     const int qrow = qt * BR + wave * 32 + qi;
     const int t = qrow < N ? qrow : N - 1;
     const int hw = wp.H * wp.W;
-    qf = t / hw;
-    qy = (t - qf * hw) / wp.W;
-    qx = t - qf * hw - qy * wp.W;
+    const int qf = t / hw;
+    const int qy = (t - qf * hw) / wp.W;
+    const int qx = t - qf * hw - qy * wp.W;
+    flo = qf - wp.rf;
+    ylo = qy - wp.rh;
+    clo = qx - wp.rw;
+    const int chi = qx + wp.rw < wp.W - 1 ? qx + wp.rw : wp.W - 1;
+    cend = chi + 1;
+    wlo = wp.W + (clo > 0 ? clo : 0);
+    wend = wp.W + chi + 1;
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) negm[i] = 0.f;
@@ -318,33 +335,63 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       }
     }
     if constexpr (WIN) {
-      // keys outside the query's window (and past N) get -inf. Lane keys come
-      // in runs of 8 consecutive tokens starting at 32kb + 16h + 8g; each run
-      // decodes its first key and steps along the column index.
+      // keys outside the query's window get -inf (keys past N already have
+      // it). Lane keys come in 4 runs of 8 consecutive tokens starting at
+      // 32kb + 16h + 8g.
       const int base = tile_at(jj) * KT;
-      const int hw = wp.H * wp.W;
+      const unsigned fspan = 2u * wp.rf, yspan = 2u * wp.rh, xspan = 2u * wp.rw;
+      if (wp.fast) {
+        // W >= 8: a run covers at most rows r0 and r0 + 1. Its visible keys
+        // form one bit range per row; the row test gates each range.
+        const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
+        auto bits = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..7
+          const int lo = a < 0 ? 0 : (a > 8 ? 8 : a);
+          const int hi = b < lo ? lo : (b > 8 ? 8 : b);
+          return (1u << hi) - (1u << lo);
+        };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k0 = base + 32 * kb + 16 * h + 8 * g;
-          int f = k0 / hw;
-          int y = (k0 - f * hw) / wp.W;
-          int x = k0 - f * hw - y * wp.W;
+          for (int h = 0; h < 2; ++h) {
+            const int k0 = base + 32 * kb + 16 * h + 8 * g;
+            const int r0 = (int)__builtin_fmaf((float)k0, wp.invW, hinvW);
+            const int c0 = k0 - __mul24(r0, wp.W);
+            const int f0 = (int)__builtin_fmaf((float)r0, wp.invH, hinvH);
+            const int y0 = r0 - __mul24(f0, wp.H);
+            const bool wrap = y0 == wp.H - 1;
+            const int y1 = wrap ? 0 : y0 + 1;
+            const int f1 = f0 + (wrap ? 1 : 0);
+            const bool row0 = ((unsigned)(f0 - flo) <= fspan) & ((unsigned)(y0 - ylo) <= yspan);
+            const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
+            const unsigned vis = (row0 ? bits(clo - c0, cend - c0) : 0u) | (row1 ? bits(wlo - c0, wend - c0) : 0u);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const bool vis = k0 + e < N && abs(f - qf) <= wp.rf && abs(y - qy) <= wp.rh && abs(x - qx) <= wp.rw;
-            if (!vis) sacc[kb][8 * h + e] = -INFINITY;
-            // next token: column + 1, carrying into row and frame
-            ++x;
-            const bool cx = x >= wp.W;
-            x = cx ? 0 : x;
-            y += cx ? 1 : 0;
-            const bool cy = y >= wp.H;
-            y = cy ? 0 : y;
-            f += cy ? 1 : 0;
+            for (int e = 0; e < 8; ++e) sacc[kb][8 * h + e] = (vis & (1u << e)) ? sacc[kb][8 * h + e] : -INFINITY;
           }
-        }
+      } else {
+        // general grid: decode each run's first key, then step the column
+        // index with carries into row and frame
+        const int hw = wp.H * wp.W;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int k0 = base + 32 * kb + 16 * h + 8 * g;
+            int f = k0 / hw;
+            int y = (k0 - f * hw) / wp.W;
+            int x = k0 - f * hw - y * wp.W;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const bool vis = ((unsigned)(f - flo) <= fspan) & ((unsigned)(y - ylo) <= yspan) &
+                               ((unsigned)(x - clo) <= xspan);
+              sacc[kb][8 * h + e] = vis ? sacc[kb][8 * h + e] : -INFINITY;
+              const bool cx = x == wp.W - 1;
+              x = cx ? 0 : x + 1;
+              const bool cy = cx & (y == wp.H - 1);
+              y = cy ? 0 : (cx ? y + 1 : y);
+              f += cy ? 1 : 0;
+            }
+          }
+      }
     }
     float ls = probs();
     if (__builtin_amdgcn_ballot_w64(!m_valid || !(ls <= kRescaleSum)) != 0) {

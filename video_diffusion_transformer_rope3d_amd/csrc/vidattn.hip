@@ -317,7 +317,7 @@ struct AttendExtras {
   int maxb = 0;
   int lists_shared = 0;  // one list per query block for every (b, head)
   bool window = false;   // mask keys outside each query's box
-  WindowParams wp{1, 1, 1, 0, 0, 0};
+  WindowParams wp{1, 1, 1, 0, 0, 0, 0, 1.f, 1.f};
 };
 
 template <int D, bool SPARSE, bool WIN>
@@ -528,7 +528,11 @@ vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, v
   // a radius at or beyond the grid extent reaches the whole axis
   const int rf = (int)std::min<int64_t>(window->r_f, window->F), rh = (int)std::min<int64_t>(window->r_h, window->H),
             rw = (int)std::min<int64_t>(window->r_w, window->W);
-  x.wp = WindowParams{(int)window->F, (int)window->H, (int)window->W, rf, rh, rw};
+  // fast key decode (see WindowParams): rows of at least 8 tokens and key
+  // indices (up to nkt * 64 - 1) below 2^22
+  const int fast = window->W >= 8 && nkt * kKT < (int64_t(1) << 22);
+  x.wp = WindowParams{(int)window->F, (int)window->H, (int)window->W, rf, rh, rw, fast,
+                      (float)(1.0 / (double)window->W), (float)(1.0 / (double)window->H)};
   if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, B * heads, N, d, softmax_scale, rp, st, x)) return s;
   return ok();
 }
