@@ -95,6 +95,34 @@ def cpu_baseline(wl, host, budget_s: float):
     }
 
 
+def gemm_context(dev, attention_tflops: float, n: int = 8192, seconds: float = 1.5):
+    """Rate of a plain bf16 matrix product (torch.mm, the vendor BLAS) on the
+    same GPU, run after the timed region: the sustained matrix-core rate of
+    this particular board under its power limit, against which the attention
+    kernel's rate can be read (boards of one model differ by several %)."""
+    import torch
+
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    flop = 2.0 * n ** 3
+    reps = max(3, int(seconds * 1.2e15 / flop))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = flop / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"op": f"torch.mm bf16 {n}x{n}x{n}", "reps": reps, "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "attention_kernel_over_gemm": round(attention_tflops / tflops, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +136,8 @@ def main() -> int:
                     help="subset: a quarter of the query tokens attend to all keys; sparse: block-sparse lists "
                          "(a band of 96 key blocks each side of the query block plus 96 global key blocks); "
                          "window: local window of radius (1, 7, 7) around each query")
+    ap.add_argument("--no-gemm-context", action="store_true",
+                    help="skip the same-box torch.mm bf16 reference rate reported after the timed region")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the timed region, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling memory counters)")
@@ -210,6 +240,9 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": committed_traffic(wl.name)},
     }
+
+    if not args.no_gemm_context:
+        result["gemm_context"] = gemm_context(dev, achieved)
 
     if not args.no_parity:
         sys.path.insert(0, os.path.join(ROOT, "tests"))

@@ -117,6 +117,45 @@ def test_workload_parity(va, wid):
     torch.cuda.empty_cache()
 
 
+def test_tensors_beyond_4_gib(va):
+    """3 x 80 heads of the 21x45x80 grid (75600 tokens), d = 128: each of Q,
+    K, V, O holds 4.6 GB and the key/value workspace 9.3 GB: (b, head) slice
+    i starts at byte i * 19.4 MB of its tensor, beyond 2^31 from i = 111 on
+    and beyond 2^32 from i = 222 on. Slices 0, 120 and 239 carry seeded inputs
+    and are checked on 256 sampled rows each; every other head is zero
+    (heads do not interact), so its output must be exactly zero."""
+    import dataclasses
+    wl = dataclasses.replace(wlmod.custom(3, 80, (21, 45, 80), 128, (44, 42, 42), seed_id=720), full_rows=False)
+    checked = [(0, 0), (1, 40), (2, 79)]
+    shape = (wl.B, wl.heads, wl.N, wl.d)
+    _log(f"large {wl.name}: {4 * wl.B * wl.heads * wl.N * wl.d * 2 / 1e9:.1f} GB of q, k, v, o")
+    dev = {n: torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for n in ("q", "k", "v")}
+    host = {}
+    for (b, h) in checked:
+        for n in ("q", "k", "v"):
+            host[(n, b, h)] = wlmod.slice_values(wl, n, b, h)
+            dev[n][b, h].copy_(parity.to_torch(host[(n, b, h)]))
+    o = va.attention(dev["q"], dev["k"], dev["v"], scale=wl.scale, grid=wl.grid, split=wl.split, theta=wl.theta)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all().item())
+    for (b, h) in [(0, 1), (1, 39), (1, 41), (2, 78)]:
+        assert o[b, h].abs().max().item() == 0.0, (b, h)
+    parts = []
+    for (b, h) in checked:
+        rows = wlmod.sample_rows(wl, b, h)
+        got = parity.from_torch(o[b, h].index_select(0, torch.from_numpy(rows).cuda()))
+        q, k, v = (oracle.decode_bf16(host[(n, b, h)]) for n in ("q", "k", "v"))
+        ref = oracle.rope_attention(q, k, v, wl.grid, wl.split, wl.theta, wl.scale, rows=rows)
+        e = np.abs(got - ref)
+        parts.append((float(e.max()), float(e.sum()), float(np.abs(ref).sum())))
+        _log(f"  head ({b}, {h}): max_abs {parts[-1][0]:.3g}, mean_rel {parts[-1][1] / parts[-1][2]:.3g}")
+    st = dict(max_abs=max(p[0] for p in parts), mean_rel=sum(p[1] for p in parts) / sum(p[2] for p in parts),
+              finite=True)
+    assert parity.within(wl, st), st
+    del o, dev
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ invariants (no oracle)
 
 def _rand(shape, dt, seed, std=0.5):
