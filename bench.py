@@ -44,6 +44,26 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def committed_counters(workload_name: str) -> dict:
+    """Matrix-core busy fraction and clock of the attention kernel from a
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel source and workload."""
+    src = kernel_source_hash()
+    for p in glob.glob(os.path.join(ROOT, "profiles", "*counters*.md")):
+        text = open(p).read()
+        m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+        m_wl = re.search(r"workload:\s*(\S+)", text)
+        if not (m_src and m_wl and m_src.group(1) == src and m_wl.group(1) == workload_name):
+            continue
+        out = {}
+        for key in ("mfma_busy_frac", "clock_ghz"):
+            m = re.search(key + r":\s*([0-9.eE+]+)", text)
+            if m:
+                out[key] = float(m.group(1))
+        return out
+    return {}
+
+
 def committed_traffic(workload_name: str):
     """HBM bytes per attention launch from a committed rocprofv3 counter
     summary, if it was taken on the current kernel source and workload."""
@@ -240,6 +260,10 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": committed_traffic(wl.name)},
     }
+    # counter-derived figures (committed rocprofv3 summaries of this kernel source, else absent)
+    if result["roofline"]["traffic"] is not None:
+        result["roofline"]["hbm_gb_s"] = round(result["roofline"]["traffic"] / (attn_mean * 1e-3) / 1e9, 1)
+    result["roofline"].update(committed_counters(wl.name))
 
     if not args.no_gemm_context:
         result["gemm_context"] = gemm_context(dev, achieved)
