@@ -277,6 +277,12 @@ WINDOW_CASES = [
     ((2, 9, 11), 128, (44, 42, 42), 2, 1, (0, 0, 0)),
     ((6, 5, 7), 128, (44, 42, 42), 1, 2, (1, 4, 2)),
     ((4, 8, 8), 64, (16, 24, 24), 1, 1, (3, 1, 0)),
+    # rows of >= 64 tokens: whole-tile test (a tile spans at most two rows)
+    ((2, 3, 63), 128, (44, 42, 42), 1, 2, (1, 1, 5)),
+    ((2, 3, 64), 128, (44, 42, 42), 1, 2, (1, 1, 5)),
+    ((2, 4, 70), 64, (16, 24, 24), 2, 1, (0, 2, 9)),
+    ((3, 2, 100), 128, (44, 42, 42), 1, 2, (1, 0, 30)),
+    ((2, 3, 129), 128, (44, 42, 42), 1, 1, (1, 1, 200)),
 ]
 
 
@@ -316,6 +322,18 @@ def test_window_unbounded_is_the_dense_attention_bitwise(va):
     b = va.attention(q, k, v, **kw)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_window_large_wide_rows(va):
+    """The 75600-token grid (21 x 45 x 80, whole-tile test) with radius
+    (1, 7, 7); 256 sampled rows of two slices."""
+    wl = wlmod.WORKLOADS[3]
+    host = parity.host_inputs(wl)
+    rows = wlmod.sample_rows(wl, 0, 0)
+    _log(f"window {wl.name} radius=(1, 7, 7)")
+    _, st = _check_window(va, wl, host, (1, 7, 7), rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)])
+    _log(f"  {st}")
+    assert _within(st), st
 
 
 def test_window_large(va):

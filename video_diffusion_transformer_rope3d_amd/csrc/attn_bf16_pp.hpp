@@ -57,15 +57,18 @@
 
 namespace vidattn {
 
-// Box of a local window over the F x H x W token grid. With fast != 0 (the
-// host sets it when W >= 8 and every key index is below 2^22) a key index k
-// is split into row k / W and column k % W as (int)fma(k, invW, invW / 2):
-// the exact quotient plus (r + 1/2) / W lies at least 1/(2W) from an integer
-// and the fp32 error stays below that for k < 2^22 (the same for row / H).
+// Box of a local window over the F x H x W token grid. With mode != 0 (the
+// host sets it when every key index is below 2^22) a key index k is split
+// into row k / W and column k % W as (int)fma(k, invW, invW / 2): the exact
+// quotient plus (r + 1/2) / W lies at least 1/(2W) from an integer and the
+// fp32 error stays below that for k < 2^22 (the same for row / H).
+// mode 2 (W >= 64): a 64-key tile spans at most two grid rows and is tested
+// as a whole; mode 1 (W >= 8): each run of 8 keys spans at most two rows;
+// mode 0: any grid, integer division and per-key stepping.
 struct WindowParams {
   int F, H, W;
   int rf, rh, rw;
-  int fast;
+  int mode;
   float invW, invH;
 };
 
@@ -340,33 +343,68 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       // 32kb + 16h + 8g.
       const int base = tile_at(jj) * KT;
       const unsigned fspan = 2u * wp.rf, yspan = 2u * wp.rh, xspan = 2u * wp.rw;
-      if (wp.fast) {
+      // score register i of key block kb takes -inf unless bit 8(2kb + i/8) + i%8
+      // of vis is set (sign-extended bit, then a bit select)
+      auto apply = [&](unsigned vis) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = 16 * kb + i;
+            const unsigned keep = (unsigned)((int)(vis << (31 - j)) >> 31);
+            const float sv = sacc[kb][i];  // (bit-casting the element expression itself reads element 0)
+            const unsigned sb = __builtin_bit_cast(unsigned, sv);
+            sacc[kb][i] = __builtin_bit_cast(float, (sb & keep) | (0xff800000u & ~keep));
+          }
+      };
+      const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
+      if (wp.mode == 2) {
+        // the tile [base, base + 64) lies in rows rb and rb + 1; the visible
+        // keys of each row form one range of tile offsets
+        auto bits64 = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..63
+          const int lo = a < 0 ? 0 : (a > 64 ? 64 : a);
+          const int hi = b < lo ? lo : (b > 64 ? 64 : b);
+          return hi == lo ? (uint64_t)0 : ((~(uint64_t)0 >> (64 - hi)) & (~(uint64_t)0 << lo));
+        };
+        const int rb = (int)__builtin_fmaf((float)base, wp.invW, hinvW);
+        const int cb = base - __mul24(rb, wp.W);
+        const int fb = (int)__builtin_fmaf((float)rb, wp.invH, hinvH);
+        const int yb = rb - __mul24(fb, wp.H);
+        const bool wrap = yb == wp.H - 1;
+        const int y1 = wrap ? 0 : yb + 1;
+        const int f1 = fb + (wrap ? 1 : 0);
+        const bool row0 = ((unsigned)(fb - flo) <= fspan) & ((unsigned)(yb - ylo) <= yspan);
+        const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
+        const uint64_t m = (row0 ? bits64(clo - cb, cend - cb) : (uint64_t)0) |
+                           (row1 ? bits64(wlo - cb, wend - cb) : (uint64_t)0);
+        // this lane's keys are the runs at tile offsets 16u + 8g (u = 2kb + h):
+        // bytes g, 2 + g, 4 + g, 6 + g of m
+        apply(__builtin_amdgcn_perm((unsigned)(m >> 32), (unsigned)m, g ? 0x07050301u : 0x06040200u));
+      } else if (wp.mode == 1) {
         // W >= 8: a run covers at most rows r0 and r0 + 1. Its visible keys
         // form one bit range per row; the row test gates each range.
-        const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
         auto bits = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..7
           const int lo = a < 0 ? 0 : (a > 8 ? 8 : a);
           const int hi = b < lo ? lo : (b > 8 ? 8 : b);
           return (1u << hi) - (1u << lo);
         };
+        unsigned vis = 0;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int k0 = base + 32 * kb + 16 * h + 8 * g;
-            const int r0 = (int)__builtin_fmaf((float)k0, wp.invW, hinvW);
-            const int c0 = k0 - __mul24(r0, wp.W);
-            const int f0 = (int)__builtin_fmaf((float)r0, wp.invH, hinvH);
-            const int y0 = r0 - __mul24(f0, wp.H);
-            const bool wrap = y0 == wp.H - 1;
-            const int y1 = wrap ? 0 : y0 + 1;
-            const int f1 = f0 + (wrap ? 1 : 0);
-            const bool row0 = ((unsigned)(f0 - flo) <= fspan) & ((unsigned)(y0 - ylo) <= yspan);
-            const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
-            const unsigned vis = (row0 ? bits(clo - c0, cend - c0) : 0u) | (row1 ? bits(wlo - c0, wend - c0) : 0u);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sacc[kb][8 * h + e] = (vis & (1u << e)) ? sacc[kb][8 * h + e] : -INFINITY;
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int k0 = base + 16 * u + 8 * g;
+          const int r0 = (int)__builtin_fmaf((float)k0, wp.invW, hinvW);
+          const int c0 = k0 - __mul24(r0, wp.W);
+          const int f0 = (int)__builtin_fmaf((float)r0, wp.invH, hinvH);
+          const int y0 = r0 - __mul24(f0, wp.H);
+          const bool wrap = y0 == wp.H - 1;
+          const int y1 = wrap ? 0 : y0 + 1;
+          const int f1 = f0 + (wrap ? 1 : 0);
+          const bool row0 = ((unsigned)(f0 - flo) <= fspan) & ((unsigned)(y0 - ylo) <= yspan);
+          const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
+          const unsigned rv = (row0 ? bits(clo - c0, cend - c0) : 0u) | (row1 ? bits(wlo - c0, wend - c0) : 0u);
+          vis |= rv << (8 * u);
+        }
+        apply(vis);
       } else {
         // general grid: decode each run's first key, then step the column
         // index with carries into row and frame

@@ -528,10 +528,11 @@ vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, v
   // a radius at or beyond the grid extent reaches the whole axis
   const int rf = (int)std::min<int64_t>(window->r_f, window->F), rh = (int)std::min<int64_t>(window->r_h, window->H),
             rw = (int)std::min<int64_t>(window->r_w, window->W);
-  // fast key decode (see WindowParams): rows of at least 8 tokens and key
-  // indices (up to nkt * 64 - 1) below 2^22
-  const int fast = window->W >= 8 && nkt * kKT < (int64_t(1) << 22);
-  x.wp = WindowParams{(int)window->F, (int)window->H, (int)window->W, rf, rh, rw, fast,
+  // key decode (see WindowParams): the fp32 split needs key indices (up to
+  // nkt * 64 - 1) below 2^22; rows of >= 64 tokens allow the whole-tile test
+  const bool small_n = nkt * kKT < (int64_t(1) << 22);
+  const int mode = !small_n ? 0 : (window->W >= 64 ? 2 : (window->W >= 8 ? 1 : 0));
+  x.wp = WindowParams{(int)window->F, (int)window->H, (int)window->W, rf, rh, rw, mode,
                       (float)(1.0 / (double)window->W), (float)(1.0 / (double)window->H)};
   if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, B * heads, N, d, softmax_scale, rp, st, x)) return s;
   return ok();
