@@ -374,26 +374,57 @@ def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
     return 0
 
 
-def window_tiles(wl, radius):
-    """Query-key pairs the window attention visits (the 64-key tiles its plan
-    lists per 256-query block, times the block's rows) and the pairs inside
-    the windows; mirrors the planning rule (whole rows of every frame in
-    range)."""
+def window_plan_lists(wl, radius):
+    """The 64-key tiles the window attention's plan lists for each 256-query
+    block, ascending (the planning rule restated: every row within r_h of a
+    row that the block's queries of a frame within r_f occupy)."""
     F, H, W = wl.grid
     hw, N = H * W, wl.N
-    rf, rh, rw = radius
-    visited = 0
+    rf, rh, _ = radius
+    lists = []
     for i in range(-(-N // 256)):
         q0, q1 = 256 * i, min(N, 256 * i + 256) - 1
         fa, fb = q0 // hw, q1 // hw
-        ya, yb = ((q0 - fa * hw) // W, (q1 - fb * hw) // W) if fa == fb else (0, H - 1)
-        f0, f1, y0, y1 = max(0, fa - rf), min(F - 1, fb + rf), max(0, ya - rh), min(H - 1, yb + rh)
-        tiles, last = 0, -1
-        for f in range(f0, f1 + 1):
-            t0, t1 = ((f * H + y0) * W) // 64, ((f * H + y1) * W + W - 1) // 64
-            tiles += max(0, t1 - max(t0, last + 1) + 1)
-            last = max(last, t1)
-        visited += tiles * 64 * (q1 - q0 + 1)
+        ya, yb = (q0 - fa * hw) // W, (q1 - fb * hw) // W
+        tiles = set()
+
+        def emit(f, lo, hi):
+            lo, hi = max(lo, 0), min(hi, H - 1)
+            if lo <= hi:
+                tiles.update(range(((f * H + lo) * W) // 64, ((f * H + hi) * W + W - 1) // 64 + 1))
+
+        for f in range(max(0, fa - rf), min(F - 1, fb + rf) + 1):
+            ga, gb = max(fa, f - rf), min(fb, f + rf)
+            if max(ga, fa + 1) <= min(gb, fb - 1):
+                emit(f, 0, H - 1)
+            elif fa == fb:
+                emit(f, ya - rh, yb + rh)
+            elif ga == fa and gb == fb:
+                if yb + rh >= ya - rh - 1:
+                    emit(f, 0, H - 1)
+                else:
+                    emit(f, 0, yb + rh)
+                    emit(f, ya - rh, H - 1)
+            elif ga == fa:
+                emit(f, ya - rh, H - 1)
+            else:
+                emit(f, 0, yb + rh)
+        lists.append(sorted(tiles))
+    return lists
+
+
+def window_plan_counts(wl, radius):
+    return [len(t) for t in window_plan_lists(wl, radius)]
+
+
+def window_tiles(wl, radius):
+    """Query-key pairs the window attention visits (the tiles its plan lists
+    per 256-query block, times the block's rows) and the pairs inside the
+    windows."""
+    F, H, W = wl.grid
+    N = wl.N
+    rf, rh, rw = radius
+    visited = sum(c * 64 * (min(N, 256 * i + 256) - 256 * i) for i, c in enumerate(window_plan_counts(wl, radius)))
     ext = lambda n, r: sum(min(n - 1, c + r) - max(0, c - r) + 1 for c in range(n))
     inside = ext(F, rf) * ext(H, rh) * ext(W, rw)
     return visited, inside
@@ -420,6 +451,14 @@ def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    # the FLOP count above restates the planning rule: check it against the
+    # tile counts the planning kernel wrote (the workspace tail starts with them)
+    base = va.vidattn_fwd_workspace_size(va.BF16, wl.B, wl.heads, wl.N, wl.d, True)
+    nqb = -(-wl.N // 256)
+    if args.warmup > 0:
+        got = wws[base:base + 4 * nqb].view(torch.int32).cpu().tolist()
+        if got != window_plan_counts(wl, radius):
+            raise RuntimeError("window plan tile counts differ from the FLOP-count rule")
     es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in es:
         a.record(stream)

@@ -324,6 +324,33 @@ def test_window_unbounded_is_the_dense_attention_bitwise(va):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_window_plan_kernel_writes_the_rule(va):
+    """The planning kernel's tile lists (in the workspace tail after a call)
+    equal the rule that bench.py counts FLOPs with, on the grids of the CPU
+    rule tests."""
+    import importlib.util
+    import os
+    from tests import test_window_plan as rule_tests
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_module", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for grid, radius in rule_tests.CASES:
+        wl = wlmod.custom(1, 1, grid, 64, (16, 24, 24), seed_id=700)
+        q, k, v = (parity.to_torch(wlmod.full(wl, n)) for n in ("q", "k", "v"))
+        n = va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, wl.N, wl.d, True)
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        va.window_attention(q, k, v, radius, grid=grid, split=wl.split, workspace=ws)
+        torch.cuda.synchronize()
+        base = va.vidattn_fwd_workspace_size(va.BF16, 1, 1, wl.N, wl.d, True)
+        nqb, nkt = -(-wl.N // 256), -(-wl.N // 64)
+        counts = ws[base:base + 4 * nqb].view(torch.int32).cpu().tolist()
+        off = base + (4 * nqb + 255) // 256 * 256
+        lists = ws[off:off + 4 * nqb * nkt].view(torch.int32).view(nqb, nkt).cpu().tolist()
+        got = [row[:c] for row, c in zip(lists, counts)]
+        assert got == bench.window_plan_lists(wl, radius), (grid, radius)
+
+
 def test_window_large_wide_rows(va):
     """The 75600-token grid (21 x 45 x 80, whole-tile test) with radius
     (1, 7, 7); 256 sampled rows of two slices."""

@@ -40,9 +40,9 @@
 // SPARSE): in the listed tiles, keys outside the box of radii (r_f, r_h,
 // r_w) around the query's grid position get -inf. Indices read from device
 // memory are clamped into range, so no input can address outside the
-// workspace. The exact step runs for a row until the row has seen a visible
-// key (in the dense case: on the first tile), so tiles whose keys are all
-// masked for some rows leave m untouched.
+// workspace. A row's m is unset until its first tile with a visible key
+// (in the dense case: the first tile); the exact step runs on that tile, so
+// tiles whose keys are all masked for a row leave its m untouched.
 #pragma once
 
 #include <type_traits>
@@ -267,6 +267,94 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     lds_barrier();
   };
 
+  // Window variant: bit 8(2kb + h) + e of window_vis(jj) is set when this
+  // lane's key 32kb + 16h + 8g + e of tile jj lies inside its query's box.
+  // It depends on the tile and the query only, so the GEMM phase folds it
+  // into the accumulator input of the first score MFMA (-m, or -inf for a
+  // key outside the box) while the matrix core runs the P.V products.
+  auto window_vis = [&](int jj) __attribute__((always_inline)) {
+    unsigned vis = 0;
+    if constexpr (WIN) {
+      const int base = tile_at(jj) * KT;
+      const unsigned fspan = 2u * wp.rf, yspan = 2u * wp.rh, xspan = 2u * wp.rw;
+      const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
+      if (wp.mode == 2) {
+        // the tile [base, base + 64) lies in rows rb and rb + 1; the visible
+        // keys of each row form one range of tile offsets
+        auto bits64 = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..63
+          const int lo = a < 0 ? 0 : (a > 64 ? 64 : a);
+          const int hi = b < lo ? lo : (b > 64 ? 64 : b);
+          return hi == lo ? (uint64_t)0 : ((~(uint64_t)0 >> (64 - hi)) & (~(uint64_t)0 << lo));
+        };
+        const int rb = (int)__builtin_fmaf((float)base, wp.invW, hinvW);
+        const int cb = base - __mul24(rb, wp.W);
+        const int fb = (int)__builtin_fmaf((float)rb, wp.invH, hinvH);
+        const int yb = rb - __mul24(fb, wp.H);
+        const bool wrap = yb == wp.H - 1;
+        const int y1 = wrap ? 0 : yb + 1;
+        const int f1 = fb + (wrap ? 1 : 0);
+        const bool row0 = ((unsigned)(fb - flo) <= fspan) & ((unsigned)(yb - ylo) <= yspan);
+        const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
+        const uint64_t m = (row0 ? bits64(clo - cb, cend - cb) : (uint64_t)0) |
+                           (row1 ? bits64(wlo - cb, wend - cb) : (uint64_t)0);
+        // this lane's keys are the runs at tile offsets 16u + 8g (u = 2kb + h):
+        // bytes g, 2 + g, 4 + g, 6 + g of m
+        vis = __builtin_amdgcn_perm((unsigned)(m >> 32), (unsigned)m, g ? 0x07050301u : 0x06040200u);
+      } else if (wp.mode == 1) {
+        // W >= 8: a run covers at most rows r0 and r0 + 1. Its visible keys
+        // form one bit range per row; the row test gates each range.
+        auto bits = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..7
+          const int lo = a < 0 ? 0 : (a > 8 ? 8 : a);
+          const int hi = b < lo ? lo : (b > 8 ? 8 : b);
+          return (1u << hi) - (1u << lo);
+        };
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k0 = base + 16 * u + 8 * g;
+          const int r0 = (int)__builtin_fmaf((float)k0, wp.invW, hinvW);
+          const int c0 = k0 - __mul24(r0, wp.W);
+          const int f0 = (int)__builtin_fmaf((float)r0, wp.invH, hinvH);
+          const int y0 = r0 - __mul24(f0, wp.H);
+          const bool wrap = y0 == wp.H - 1;
+          const int y1 = wrap ? 0 : y0 + 1;
+          const int f1 = f0 + (wrap ? 1 : 0);
+          const bool row0 = ((unsigned)(f0 - flo) <= fspan) & ((unsigned)(y0 - ylo) <= yspan);
+          const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
+          const unsigned rv = (row0 ? bits(clo - c0, cend - c0) : 0u) | (row1 ? bits(wlo - c0, wend - c0) : 0u);
+          vis |= rv << (8 * u);
+        }
+      } else {
+        // general grid: decode each run's first key, then step the column
+        // index with carries into row and frame
+        const int hw = wp.H * wp.W;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k0 = base + 16 * u + 8 * g;
+          int f = k0 / hw;
+          int y = (k0 - f * hw) / wp.W;
+          int x = k0 - f * hw - y * wp.W;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool in = ((unsigned)(f - flo) <= fspan) & ((unsigned)(y - ylo) <= yspan) &
+                            ((unsigned)(x - clo) <= xspan);
+            vis |= (in ? 1u : 0u) << (8 * u + e);
+            const bool cx = x == wp.W - 1;
+            x = cx ? 0 : x + 1;
+            const bool cy = cx & (y == wp.H - 1);
+            y = cy ? 0 : (cx ? y + 1 : y);
+            f += cy ? 1 : 0;
+          }
+        }
+      }
+    }
+    return vis;
+  };
+
+  // window bits of the tile whose scores the last GEMM phase produced (the
+  // softmax phase that follows reads them); all keys count as visible
+  // outside the window variant
+  unsigned wvis = ~0u;
+
   // GEMM phase of tile jj: O^T += V_{jj-1}^T P^T (PV), S'^T = K_jj Q'^T - m (SC).
   // The operands (16 B per lane each) stream from LDS in batches of RB,
   // double-buffered in registers: batch b+1 is read while the MFMAs of
@@ -285,6 +373,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     static_assert(NOP % RB == 0, "operand batches");
     // operand i < NV: V block (db, ms) = i; else K block (kb, s) = i - NV
     auto addr = [&](int i) __attribute__((always_inline)) { return st + (i < NV ? TILE + i * 1024 : (i - NV) * 1024); };
+    // accumulator input of the first score MFMA per key block: -m, or -inf
+    // for a key outside the window (sign-extended bit, then a bit select)
+    f32x16 cneg[2];
+    if constexpr (WIN && decltype(SC)::value) {
+      const unsigned vis = window_vis(jj);
+      wvis = vis;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const unsigned keep = (unsigned)((int)(vis << (31 - (16 * kb + i))) >> 31);
+          const float mv = negm[i];  // (bit-casting the element expression itself reads element 0)
+          const unsigned mb = __builtin_bit_cast(unsigned, mv);
+          cneg[kb][i] = __builtin_bit_cast(float, (mb & keep) | (0xff800000u & ~keep));
+        }
+    }
     u32x4 buf[2][RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) buf[0][r] = *reinterpret_cast<const u32x4*>(addr(r));
@@ -310,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         } else {
           const int kb = (i - NV) / KSTEPS, s = (i - NV) % KSTEPS;
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), qreg[s],
-                                                            s == 0 ? negm : sacc[kb], 0, 0, 0);
+                                                            s == 0 ? (WIN ? cneg[kb] : negm) : sacc[kb], 0, 0, 0);
         }
       }
     }
@@ -337,102 +441,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           }
       }
     }
-    if constexpr (WIN) {
-      // keys outside the query's window get -inf (keys past N already have
-      // it). Lane keys come in 4 runs of 8 consecutive tokens starting at
-      // 32kb + 16h + 8g.
-      const int base = tile_at(jj) * KT;
-      const unsigned fspan = 2u * wp.rf, yspan = 2u * wp.rh, xspan = 2u * wp.rw;
-      // score register i of key block kb takes -inf unless bit 8(2kb + i/8) + i%8
-      // of vis is set (sign-extended bit, then a bit select)
-      auto apply = [&](unsigned vis) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = 16 * kb + i;
-            const unsigned keep = (unsigned)((int)(vis << (31 - j)) >> 31);
-            const float sv = sacc[kb][i];  // (bit-casting the element expression itself reads element 0)
-            const unsigned sb = __builtin_bit_cast(unsigned, sv);
-            sacc[kb][i] = __builtin_bit_cast(float, (sb & keep) | (0xff800000u & ~keep));
-          }
-      };
-      const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
-      if (wp.mode == 2) {
-        // the tile [base, base + 64) lies in rows rb and rb + 1; the visible
-        // keys of each row form one range of tile offsets
-        auto bits64 = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..63
-          const int lo = a < 0 ? 0 : (a > 64 ? 64 : a);
-          const int hi = b < lo ? lo : (b > 64 ? 64 : b);
-          return hi == lo ? (uint64_t)0 : ((~(uint64_t)0 >> (64 - hi)) & (~(uint64_t)0 << lo));
-        };
-        const int rb = (int)__builtin_fmaf((float)base, wp.invW, hinvW);
-        const int cb = base - __mul24(rb, wp.W);
-        const int fb = (int)__builtin_fmaf((float)rb, wp.invH, hinvH);
-        const int yb = rb - __mul24(fb, wp.H);
-        const bool wrap = yb == wp.H - 1;
-        const int y1 = wrap ? 0 : yb + 1;
-        const int f1 = fb + (wrap ? 1 : 0);
-        const bool row0 = ((unsigned)(fb - flo) <= fspan) & ((unsigned)(yb - ylo) <= yspan);
-        const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
-        const uint64_t m = (row0 ? bits64(clo - cb, cend - cb) : (uint64_t)0) |
-                           (row1 ? bits64(wlo - cb, wend - cb) : (uint64_t)0);
-        // this lane's keys are the runs at tile offsets 16u + 8g (u = 2kb + h):
-        // bytes g, 2 + g, 4 + g, 6 + g of m
-        apply(__builtin_amdgcn_perm((unsigned)(m >> 32), (unsigned)m, g ? 0x07050301u : 0x06040200u));
-      } else if (wp.mode == 1) {
-        // W >= 8: a run covers at most rows r0 and r0 + 1. Its visible keys
-        // form one bit range per row; the row test gates each range.
-        auto bits = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..7
-          const int lo = a < 0 ? 0 : (a > 8 ? 8 : a);
-          const int hi = b < lo ? lo : (b > 8 ? 8 : b);
-          return (1u << hi) - (1u << lo);
-        };
-        unsigned vis = 0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k0 = base + 16 * u + 8 * g;
-          const int r0 = (int)__builtin_fmaf((float)k0, wp.invW, hinvW);
-          const int c0 = k0 - __mul24(r0, wp.W);
-          const int f0 = (int)__builtin_fmaf((float)r0, wp.invH, hinvH);
-          const int y0 = r0 - __mul24(f0, wp.H);
-          const bool wrap = y0 == wp.H - 1;
-          const int y1 = wrap ? 0 : y0 + 1;
-          const int f1 = f0 + (wrap ? 1 : 0);
-          const bool row0 = ((unsigned)(f0 - flo) <= fspan) & ((unsigned)(y0 - ylo) <= yspan);
-          const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
-          const unsigned rv = (row0 ? bits(clo - c0, cend - c0) : 0u) | (row1 ? bits(wlo - c0, wend - c0) : 0u);
-          vis |= rv << (8 * u);
-        }
-        apply(vis);
-      } else {
-        // general grid: decode each run's first key, then step the column
-        // index with carries into row and frame
-        const int hw = wp.H * wp.W;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int k0 = base + 32 * kb + 16 * h + 8 * g;
-            int f = k0 / hw;
-            int y = (k0 - f * hw) / wp.W;
-            int x = k0 - f * hw - y * wp.W;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const bool vis = ((unsigned)(f - flo) <= fspan) & ((unsigned)(y - ylo) <= yspan) &
-                               ((unsigned)(x - clo) <= xspan);
-              sacc[kb][8 * h + e] = vis ? sacc[kb][8 * h + e] : -INFINITY;
-              const bool cx = x == wp.W - 1;
-              x = cx ? 0 : x + 1;
-              const bool cy = cx & (y == wp.H - 1);
-              y = cy ? 0 : (cx ? y + 1 : y);
-              f += cy ? 1 : 0;
-            }
-          }
-      }
-    }
     float ls = probs();
-    if (__builtin_amdgcn_ballot_w64(!m_valid || !(ls <= kRescaleSum)) != 0) {
+    // the exact step: for a row's first tile with a visible key (a row with
+    // no visible key in this tile keeps m unset), and when the sum shows a
+    // score far above m
+    if (__builtin_amdgcn_ballot_w64((!m_valid && wvis != 0u) || !(ls <= kRescaleSum)) != 0) {
       // exact maximum of the tile (relative to the current m); a row that
       // has seen no visible key yet takes the tile's maximum as its m (and
       // keeps m = 0 if the tile shows it none)
