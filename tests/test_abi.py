@@ -213,3 +213,20 @@ def test_single_hip_runtime_whatever_the_import_order():
             "r = va._loaded_hip_runtimes(); print(len(r)); assert len(r) == 1, r")
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
+
+
+def test_library_imports_no_allocation_copy_or_sync():
+    """The library allocates, copies and synchronizes nothing: of the HIP
+    runtime it imports only kernel registration, launch and error strings."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", va.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    hip = sorted({line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()})
+    allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+               "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipGetErrorString", "hipGetLastError",
+               "hipLaunchKernel"}
+    assert set(hip) <= allowed, sorted(set(hip) - allowed)

@@ -156,6 +156,28 @@ def test_tensors_beyond_4_gib(va):
     torch.cuda.empty_cache()
 
 
+def test_no_device_memory_beyond_the_buffers(va):
+    """A call on the 2 x 10 heads x 75600-token workload, with the output and
+    workspace supplied, leaves the device's free memory unchanged: nothing
+    of the 75600^2 scores per head (23 GB in fp32) is ever stored."""
+    wl = wlmod.WORKLOADS[3]
+    shape = (wl.B, wl.heads, wl.N, wl.d)
+    q, k, v = (torch.randn(shape, device="cuda").mul_(0.5).to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(q)
+    ws = va.workspace_for(q, True)
+    kw = dict(scale=wl.scale, grid=wl.grid, split=wl.split, theta=wl.theta, out=o, workspace=ws)
+    va.attention(q, k, v, **kw)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    peak0 = torch.cuda.max_memory_allocated()
+    va.attention(q, k, v, **kw)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
+    assert torch.cuda.max_memory_allocated() == peak0
+    assert ws.numel() == 4 * wl.B * wl.heads * (-(-wl.N // 64) * 64) * wl.d
+
+
 # ------------------------------------------------------------------ invariants (no oracle)
 
 def _rand(shape, dt, seed, std=0.5):
