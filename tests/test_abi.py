@@ -85,6 +85,8 @@ def fwd(q=Q, k=K, v=V, o=O, dt=va.BF16, B=2, H=40, N=N5, d=128, scale=0.088, rop
     (dict(o=Q), 1, "overlap"),
     (dict(o=WS), 1, "overlap"),
     (dict(B=1 << 40), 1, "overflow"),
+    (dict(N=(1 << 24) + 1, rope=None), 2, "exceeds"),
+    (dict(B=1 << 11, H=1 << 10), 1, "exceeds"),
 ])
 def test_fwd_rejects(kw, status, needle):
     s, msg = fwd(**kw)

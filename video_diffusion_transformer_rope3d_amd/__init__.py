@@ -30,8 +30,8 @@ SPARSE_Q_BLOCK, SPARSE_K_BLOCK = 256, 64  # VIDATTN_SPARSE_Q_BLOCK, VIDATTN_SPAR
 
 EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend",
                     "vidattn_fwd_attend_subset", "vidattn_fwd_attend_block_sparse", "vidattn_fwd_window",
-                    "vidattn_fwd_window_workspace_size", "vidattn_fwd_workspace_size", "vidattn_status_string", "vidattn_last_error",
-                    "vidattn_abi_version")
+                    "vidattn_fwd_window_workspace_size", "vidattn_fwd_workspace_size", "vidattn_status_string",
+                    "vidattn_last_error", "vidattn_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
