@@ -237,9 +237,9 @@ typedef struct {
  * Sparse Forcing (its abstract on thelatestinai.com/papers/2606.17566); the
  * pages fix no window shape, the centred box above is the plainest reading.
  * One call runs the key/value pre-pass, a planning kernel that lists per
- * 256-query block the 64-key tiles meeting its queries' windows (in the
- * workspace), and the attention over those tiles with the keys outside each
- * query's box masked. Arguments as for vidattn_fwd, plus:
+ * 256-query block the 64-key tiles of the grid rows its queries' windows
+ * reach (in the workspace), and the attention over those tiles with the keys
+ * outside each query's box masked. Arguments as for vidattn_fwd, plus:
  *   window     non-null; its grid must equal rope's when rope is given.
  *   workspace  at least vidattn_fwd_window_workspace_size(...) bytes.
  * An unbounded window gives the vidattn_fwd result bit for bit. Only BF16 is
