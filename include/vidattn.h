@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define VIDATTN_ABI_VERSION 3
+#define VIDATTN_ABI_VERSION 4
 
 typedef enum {
   VIDATTN_OK = 0,
@@ -110,6 +110,23 @@ typedef struct {
 vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt,
                               int64_t B, int64_t heads, int64_t d, const vidattn_rope3d_desc* rope,
                               float prescale, void* hip_stream);
+
+/* The same rotation for a contiguous run of tokens of the grid: row r of
+ * each (b, head) slice is grid token token_offset + r, and turns by that
+ * token's position. This is the rotation of one GPU's sequence shard before
+ * the all-to-all of Ulysses sequence parallelism (the vidax summary,
+ * paperlayer.ai/abs/2609.18077v1, section 2, heading "Spatiotemporal tensor
+ * and sequence sharding": tokens are partitioned across devices and
+ * all-to-all transposes give head-sharded views for attention), so that
+ * every shard uses global positions.
+ *   in, out      [B][heads][n_tokens][d]; dtypes, overlap, prescale and d
+ *                as for vidattn_rope3d.
+ *   n_tokens     >= 1; token_offset >= 0 and token_offset + n_tokens <=
+ *                F*H*W (else INVALID_ARG).
+ * Offset 0 with n_tokens = F*H*W is vidattn_rope3d, bit for bit. */
+vidattn_status vidattn_rope3d_tokens(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt,
+                                     int64_t B, int64_t heads, int64_t n_tokens, int64_t token_offset, int64_t d,
+                                     const vidattn_rope3d_desc* rope, float prescale, void* hip_stream);
 
 /* Attention forward: o = softmax(scale * rot(q) rot(k)^T) v per (b, head).
  *   q, k, v, o    [B][heads][N][d], dtype dt (BF16 or F32); o has dtype dt.

@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_strings():
-    assert va.vidattn_abi_version() == 3
+    assert va.vidattn_abi_version() == 4
     for s, txt in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "workspace too small"),
                    (4, "HIP error")]:
         assert va.vidattn_status_string(s) == txt
@@ -122,6 +122,21 @@ def test_rope_rejects(kw, status, needle):
     s, msg = rope_call(**kw)
     assert s == status, (s, msg)
     assert needle in msg
+
+
+def test_rope3d_tokens_rejects():
+    """The token-offset rotation validates the token range against the grid
+    (and everything vidattn_rope3d validates) before any HIP call."""
+    def rt(n=100, off=0, d=128, rope=GOOD, inp=Q, out=O):
+        return va.vidattn_rope3d_tokens(inp, va.BF16, out, va.BF16, 2, 40, n, off, d, rope, 1.0, None)
+    for kw in (dict(n=0), dict(n=-1), dict(off=-1), dict(off=N5 - 99), dict(n=N5 + 1), dict(off=1 << 40),
+               dict(n=N5, off=1)):
+        assert rt(**kw) == 1, kw
+        assert "outside" in va.vidattn_last_error(), (kw, va.vidattn_last_error())
+    assert rt(inp=None) == 1 and "non-null" in va.vidattn_last_error()
+    assert rt(d=100) == 2
+    assert rt(rope=Rope3dDesc.make((0, 45, 80), (44, 42, 42))) == 1 and "extents" in va.vidattn_last_error()
+    assert rt(out=Q + 16) == 1 and "overlap" in va.vidattn_last_error()
 
 
 def test_last_error_is_per_call():

@@ -57,6 +57,37 @@ def test_rope3d_standalone(va, in_dt, out_dt, shape):
     assert np.all(err <= tol), float(np.max(err - tol))
 
 
+@pytest.mark.parametrize("grid,d,split,shards", [
+    ((3, 5, 7), 128, (44, 42, 42), [(0, 105), (0, 1), (17, 40), (104, 1), (60, 45)]),
+    ((21, 30, 52), 64, (16, 24, 24), [(0, 8190), (8190, 8190), (24570, 8190), (32000, 760), (12345, 6789)]),
+])
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f32", "f32")])
+def test_rope3d_token_shards(va, grid, d, split, shards, in_dt, out_dt):
+    """A run of tokens rotated with its global positions (a sequence shard):
+    against the oracle at those positions, and bit for bit the matching rows
+    of the whole-grid rotation."""
+    wl = wlmod.custom(2, 3, grid, d, split, dtype=in_dt, seed_id=310, std=(1.0, 1.0, 1.0))
+    _log(f"rope3d shards {in_dt}->{out_dt} grid={grid} d={d}")
+    x_h = wlmod.full(wl, "q")
+    x = parity.to_torch(x_h)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[out_dt]
+    whole = va.rope3d(x, grid, split, wl.theta, out_dtype=tdt, prescale=0.75)
+    pos = oracle.grid_positions(grid)
+    for off, n in shards:
+        part = va.rope3d(x[:, :, off:off + n].contiguous(), grid, split, wl.theta, token_offset=off, out_dtype=tdt,
+                         prescale=0.75)
+        torch.cuda.synchronize()
+        assert torch.equal(part.view(torch.int16) if tdt == torch.bfloat16 else part,
+                           whole[:, :, off:off + n].view(torch.int16) if tdt == torch.bfloat16
+                           else whole[:, :, off:off + n]), (off, n)
+        got = parity.from_torch(part)
+        ref = oracle.rope3d_at(parity.decode(wl, x_h[:, :, off:off + n]), pos[off:off + n], split, wl.theta) * 0.75
+        err = np.abs(got - ref)
+        mag = 1.0 + np.abs(ref)
+        tol = 2e-6 * mag if out_dt == "f32" else 0.5 * _ulp(ref, 7) + 2e-6 * mag
+        assert np.all(err <= tol), (off, n, float(np.max(err - tol)))
+
+
 def test_rope3d_in_place_matches_out_of_place(va):
     wl = wlmod.custom(1, 2, (5, 6, 7), 128, (44, 42, 42), seed_id=301)
     x = parity.to_torch(wlmod.full(wl, "k"))

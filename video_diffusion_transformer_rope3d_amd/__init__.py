@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "BF16", "F16", "F32", "VidattnError", "Rope3dDesc", "lib_path", "load",
-    "vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend", "vidattn_fwd_attend_subset",
+    "vidattn_rope3d", "vidattn_rope3d_tokens", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend", "vidattn_fwd_attend_subset",
     "vidattn_fwd_attend_block_sparse", "vidattn_fwd_workspace_size", "vidattn_status_string",
     "vidattn_last_error", "vidattn_abi_version", "attention", "prepare", "attend", "attend_subset",
     "attend_block_sparse", "rope3d", "workspace_for", "SPARSE_Q_BLOCK", "SPARSE_K_BLOCK", "EXPORTED_SYMBOLS",
@@ -24,11 +24,12 @@ __all__ = [
 
 BF16, F16, F32 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 SPARSE_Q_BLOCK, SPARSE_K_BLOCK = 256, 64  # VIDATTN_SPARSE_Q_BLOCK, VIDATTN_SPARSE_K_BLOCK
 
-EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_fwd", "vidattn_fwd_prepare", "vidattn_fwd_attend",
+EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_rope3d_tokens", "vidattn_fwd", "vidattn_fwd_prepare",
+                    "vidattn_fwd_attend",
                     "vidattn_fwd_attend_subset", "vidattn_fwd_attend_block_sparse", "vidattn_fwd_window",
                     "vidattn_fwd_window_workspace_size", "vidattn_fwd_workspace_size", "vidattn_status_string",
                     "vidattn_last_error", "vidattn_abi_version")
@@ -115,6 +116,9 @@ def load() -> ctypes.CDLL:
     lib.vidattn_rope3d.restype = ctypes.c_int
     lib.vidattn_rope3d.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64,
                                    ctypes.POINTER(Rope3dDesc), ctypes.c_float, vp]
+    lib.vidattn_rope3d_tokens.restype = ctypes.c_int
+    lib.vidattn_rope3d_tokens.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, i64, i64,
+                                          ctypes.POINTER(Rope3dDesc), ctypes.c_float, vp]
     lib.vidattn_fwd.restype = ctypes.c_int
     lib.vidattn_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                 ctypes.POINTER(Rope3dDesc), vp, sz, vp]
@@ -158,6 +162,12 @@ def _status_text(s: int) -> str:
 def vidattn_rope3d(inp, in_dt, out, out_dt, B, heads, d, rope, prescale=1.0, stream=None) -> int:
     return load().vidattn_rope3d(inp, in_dt, out, out_dt, B, heads, d,
                                  ctypes.byref(rope) if rope is not None else None, prescale, stream)
+
+
+def vidattn_rope3d_tokens(inp, in_dt, out, out_dt, B, heads, n_tokens, token_offset, d, rope, prescale=1.0,
+                          stream=None) -> int:
+    return load().vidattn_rope3d_tokens(inp, in_dt, out, out_dt, B, heads, n_tokens, token_offset, d,
+                                        ctypes.byref(rope) if rope is not None else None, prescale, stream)
 
 
 def vidattn_fwd(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, workspace, workspace_bytes,
@@ -386,18 +396,27 @@ def window_attention(q, k, v, radius, *, grid, split=None, theta=10000.0, scale=
     return out
 
 
-def rope3d(x, grid, split, theta=10000.0, *, out=None, out_dtype=None, prescale=1.0, stream=None):
-    """3D rotary embedding of a [B, heads, N, d] tensor (out may be x)."""
+def rope3d(x, grid, split, theta=10000.0, *, token_offset=None, out=None, out_dtype=None, prescale=1.0,
+           stream=None):
+    """3D rotary embedding of a [B, heads, n, d] tensor (out may be x). With
+    token_offset, row r is grid token token_offset + r (a sequence shard);
+    without it, x holds the whole grid."""
     torch = _torch()
     B, H, N, d = x.shape
     if not x.is_contiguous():
         raise ValueError("x must be contiguous")
-    if N != int(grid[0]) * int(grid[1]) * int(grid[2]):
-        raise ValueError(f"x has {N} tokens, grid {tuple(grid)} has {int(grid[0]) * int(grid[1]) * int(grid[2])}")
+    n_grid = int(grid[0]) * int(grid[1]) * int(grid[2])
+    if token_offset is None and N != n_grid:
+        raise ValueError(f"x has {N} tokens, grid {tuple(grid)} has {n_grid}")
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    _raise(vidattn_rope3d(x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), B, H, d,
-                          Rope3dDesc.make(grid, split, theta), prescale, _stream(stream)))
+    desc = Rope3dDesc.make(grid, split, theta)
+    if token_offset is None:
+        _raise(vidattn_rope3d(x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), B, H, d, desc, prescale,
+                              _stream(stream)))
+    else:
+        _raise(vidattn_rope3d_tokens(x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), B, H, N, int(token_offset), d,
+                                     desc, prescale, _stream(stream)))
     return out
 
 

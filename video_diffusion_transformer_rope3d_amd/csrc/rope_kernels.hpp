@@ -66,9 +66,10 @@ struct Elem8<float> {
 
 // One thread = one 8-element chunk (4 pairs) of one token; its 4 cos/sin
 // pairs are evaluated once and reused over `bh_per_block` (batch, head)
-// slices. grid = (ceil(N*d/8 / 256), ceil(B*heads / bh_per_block)).
+// slices. Row n of each slice (n < N) is grid token n0 + n.
+// grid = (ceil(N*d/8 / 256), ceil(B*heads / bh_per_block)).
 template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void rope3d_kernel(const TIn* in, TOut* out, int64_t nbh, int N, int d,
+__global__ __launch_bounds__(256) void rope3d_kernel(const TIn* in, TOut* out, int64_t nbh, int N, int n0, int d,
                                                      float prescale, int bh_per_block, RopeParams rp) {
   const int cpt = d >> 3;
   const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void rope3d_kernel(const TIn* in, TOut* out, i
   const int c = (int)(item - (int64_t)n * cpt);
   float cs[4], sn[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) rope_cos_sin(rp, n, 4 * c + j, cs[j], sn[j]);
+  for (int j = 0; j < 4; ++j) rope_cos_sin(rp, n0 + n, 4 * c + j, cs[j], sn[j]);
   const int64_t bh0 = (int64_t)blockIdx.y * bh_per_block;
   const int64_t bh1 = bh0 + bh_per_block < nbh ? bh0 + bh_per_block : nbh;
   for (int64_t bh = bh0; bh < bh1; ++bh) {

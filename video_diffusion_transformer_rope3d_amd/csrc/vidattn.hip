@@ -154,9 +154,16 @@ size_t vidattn_fwd_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, in
   return 0;
 }
 
-vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt, int64_t B,
-                              int64_t heads, int64_t d, const vidattn_rope3d_desc* rope, float prescale,
-                              void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The standalone rotation of n_tokens rows per (b, head) that are grid tokens
+// token_offset .. token_offset + n_tokens - 1 (the whole grid: offset 0,
+// F*H*W rows).
+vidattn_status rope3d_rows(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt, int64_t B,
+                           int64_t heads, int64_t n_tokens, int64_t token_offset, int64_t d,
+                           const vidattn_rope3d_desc* rope, float prescale, void* hip_stream) {
   if (!in || !out || !rope) return fail(VIDATTN_ERR_INVALID_ARG, "in, out and rope must be non-null");
   if (!aligned16(in) || !aligned16(out)) return fail(VIDATTN_ERR_INVALID_ARG, "in and out must be 16-byte aligned");
   if (in_dt != VIDATTN_BF16 && in_dt != VIDATTN_F32)
@@ -172,7 +179,11 @@ vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vi
     return fail(VIDATTN_ERR_UNSUPPORTED, "head dim %lld: rotation supports multiples of 8 up to 256", (long long)d);
   if (vidattn_status s = check_rope(rope, d, 0, false)) return s;
   if (!std::isfinite(prescale)) return fail(VIDATTN_ERR_INVALID_ARG, "prescale must be finite");
-  const int64_t N = rope->F * rope->H * rope->W;
+  const int64_t grid_n = rope->F * rope->H * rope->W;
+  if (n_tokens < 1 || token_offset < 0 || token_offset > grid_n - n_tokens)
+    return fail(VIDATTN_ERR_INVALID_ARG, "tokens %lld .. %lld + %lld lie outside the %lld-token grid",
+                (long long)token_offset, (long long)token_offset, (long long)n_tokens, (long long)grid_n);
+  const int64_t N = n_tokens;
   int64_t elems, bytes_in, bytes_out;
   if (!mul_ok(nbh, N * d, &elems) || !mul_ok(elems, (int64_t)dtype_size(in_dt), &bytes_in) ||
       !mul_ok(elems, (int64_t)dtype_size(out_dt), &bytes_out))
@@ -192,7 +203,7 @@ vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vi
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
 #define VIDATTN_ROPE_LAUNCH(TI, TO)                                                                                 \
   hipLaunchKernelGGL((rope3d_kernel<TI, TO>), grid, dim3(256), 0, st, static_cast<const TI*>(in),                  \
-                     static_cast<TO*>(out), nbh, (int)N, (int)d, prescale, grp, rp)
+                     static_cast<TO*>(out), nbh, (int)N, (int)token_offset, (int)d, prescale, grp, rp)
   if (in_dt == VIDATTN_BF16) {
     if (out_dt == VIDATTN_BF16) VIDATTN_ROPE_LAUNCH(uint16_t, uint16_t);
     else if (out_dt == VIDATTN_F16) VIDATTN_ROPE_LAUNCH(uint16_t, _Float16);
@@ -205,6 +216,27 @@ vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vi
 #undef VIDATTN_ROPE_LAUNCH
   if (vidattn_status s = hip_check("rope3d launch")) return s;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+vidattn_status vidattn_rope3d(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt, int64_t B,
+                              int64_t heads, int64_t d, const vidattn_rope3d_desc* rope, float prescale,
+                              void* hip_stream) {
+  // the whole grid (a malformed descriptor is reported by the shared checks)
+  int64_t hw = 0, n = 0;
+  if (rope && rope->F >= 1 && rope->H >= 1 && rope->W >= 1 &&
+      !(mul_ok(rope->H, rope->W, &hw) && mul_ok(rope->F, hw, &n)))
+    n = 0;
+  return rope3d_rows(in, in_dt, out, out_dt, B, heads, n, 0, d, rope, prescale, hip_stream);
+}
+
+vidattn_status vidattn_rope3d_tokens(const void* in, vidattn_dtype in_dt, void* out, vidattn_dtype out_dt, int64_t B,
+                                     int64_t heads, int64_t n_tokens, int64_t token_offset, int64_t d,
+                                     const vidattn_rope3d_desc* rope, float prescale, void* hip_stream) {
+  return rope3d_rows(in, in_dt, out, out_dt, B, heads, n_tokens, token_offset, d, rope, prescale, hip_stream);
 }
 
 }  // extern "C"
@@ -302,7 +334,7 @@ vidattn_status launch_prepare(const void* k, const void* v, vidattn_dtype dt, in
   const int grp = bh_group(xblocks, nbh);
   const dim3 grid((unsigned)xblocks, (unsigned)((nbh + grp - 1) / grp));
   hipLaunchKernelGGL((rope3d_kernel<float, float>), grid, dim3(256), 0, st, static_cast<const float*>(k),
-                     static_cast<float*>(workspace), nbh, (int)N, (int)d, 1.0f, grp, rp);
+                     static_cast<float*>(workspace), nbh, (int)N, 0, (int)d, 1.0f, grp, rp);
   return hip_check("f32 key rotation launch");
 }
 
