@@ -23,6 +23,7 @@ from .reference import (  # noqa: F401
     grid_positions,
     pair_frequencies,
     rope3d,
+    block_mask_attention,
     block_sparse_attention,
     block_sparse_mask,
     rope3d_at,

@@ -204,6 +204,36 @@ def block_sparse_attention(q, k, v, grid, split, theta, scale, kv_blocks, kv_cou
     return out
 
 
+def block_mask_attention(q, k, v, grid, split, theta, scale, mask, q_block=256, k_block=64, rows=None) -> np.ndarray:
+    """Block-sparse attention driven by a bit mask (the per-head block mask of
+    ScalingAttention's bit-wise block-sparse kernel, its abstract on
+    thelatestinai.com/papers/2606.17566): query token i sees key token j when
+    mask[i // q_block, j // k_block] is true; logits of the other keys are
+    -inf before the softmax, and a query that sees no key outputs 0 (the same
+    reading as block_sparse_attention). mask is a boolean (nqb, nkb) array of
+    one (batch, head) slice; q, k, v are (N, d) before rotation."""
+    N = np.asarray(q).shape[0]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    mask = np.asarray(mask, dtype=bool)
+    q = np.asarray(q, np.float64)[rows]
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    if grid is not None:
+        pos = grid_positions(grid)
+        q = rope3d_at(q, pos[rows], split, theta)
+        k = rope3d_at(k, pos, split, theta)
+    key_block = np.arange(N) // k_block
+    out = np.zeros((rows.shape[0], v.shape[1]), dtype=np.float64)
+    for n, i in enumerate(rows):
+        seen = mask[i // q_block, key_block]
+        if not seen.any():
+            continue
+        s = float(scale) * (k[seen] @ q[n])
+        e = np.exp(s - s.max())
+        out[n] = (e / e.sum()) @ v[seen]
+    return out
+
+
 # ---------------------------------------------------------------- local-window attention
 
 def window_visible(grid, radius, rows=None) -> np.ndarray:

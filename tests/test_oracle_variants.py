@@ -293,3 +293,65 @@ def test_window_harness_without_mistake_is_the_oracle():
     exact = _window_with(lambda p, r: np.all(np.abs(p[:, None] - p[None]) <= r, axis=2))
     _close(exact(q, k, v, GRID, SPLIT, THETA, SCALE, (1, 1, 2)),
            reference.window_attention(q, k, v, GRID, SPLIT, THETA, SCALE, (1, 1, 2)), 1e-14, "harness")
+
+
+# ---------------------------------------------------------------- block-sparse attention from a bit mask
+
+def _mask_from_lists(blocks, count, nkb):
+    m = np.zeros((len(count), nkb), dtype=bool)
+    for i, c in enumerate(count):
+        m[i, blocks[i, :c]] = True
+    return m
+
+
+def mask_pins(fn):
+    """Pins of block_mask_attention (fn has its signature)."""
+    q, k, v = _data(21)
+    nqb, nkb = -(-N // QB), -(-N // KB)
+    # against the pure-Python brute force, with the mask's set bits as lists
+    blocks, count = _lists(22, nqb, nkb, 3)
+    count[0] = max(count[0], 1)
+    mask = _mask_from_lists(blocks, count, nkb)
+    _close(fn(q, k, v, GRID, SPLIT, THETA, SCALE, mask, QB, KB),
+           brute.block_sparse_attend(q.tolist(), k.tolist(), v.tolist(), GRID, SPLIT, THETA, SCALE,
+                                     blocks.tolist(), count.tolist(), QB, KB), 1e-12, "bit mask vs brute force")
+    # every bit set: the dense attention
+    _close(fn(q, k, v, GRID, SPLIT, THETA, SCALE, np.ones((nqb, nkb), dtype=bool), QB, KB),
+           reference.rope_attention(q, k, v, GRID, SPLIT, THETA, SCALE), 1e-12, "full mask vs dense")
+    # a query block whose row is empty outputs 0; an asymmetric pattern
+    m = np.zeros((nqb, nkb), dtype=bool)
+    m[0, 1] = True
+    m[2, 0] = m[2, 3] = True
+    out = fn(q, k, v, GRID, SPLIT, THETA, SCALE, m, QB, KB)
+    _close(out[QB:2 * QB], np.zeros((QB, D)), 0.0, "empty mask row")
+    _close(out, brute.block_sparse_attend(q.tolist(), k.tolist(), v.tolist(), GRID, SPLIT, THETA, SCALE,
+                                          [[1, 0], [0, 0], [0, 3]], [1, 0, 2], QB, KB), 1e-12, "asymmetric mask")
+
+
+def test_block_mask_pins():
+    mask_pins(reference.block_mask_attention)
+
+
+def _mask_mutant(transpose=False, swap_blocks=False, invert=False):
+    def fn(q, k, v, grid, split, theta, scale, mask, q_block=256, k_block=64, rows=None):
+        m = np.asarray(mask, dtype=bool)
+        if invert:
+            m = ~m
+        if transpose:
+            full = np.zeros((max(m.shape), max(m.shape)), dtype=bool)
+            full[:m.shape[0], :m.shape[1]] = m
+            m = full.T[:m.shape[0], :m.shape[1]]
+        qb, kb = (k_block, q_block) if swap_blocks else (q_block, k_block)
+        nq = -(-np.asarray(q).shape[0] // qb)
+        nk = -(-np.asarray(q).shape[0] // kb)
+        mm = np.zeros((nq, nk), dtype=bool)
+        mm[:min(nq, m.shape[0]), :min(nk, m.shape[1])] = m[:nq, :nk]
+        return reference.block_mask_attention(q, k, v, grid, split, theta, scale, mm, qb, kb, rows)
+    return fn
+
+
+@pytest.mark.parametrize("mutant", [dict(transpose=True), dict(swap_blocks=True), dict(invert=True)],
+                         ids=lambda m: next(iter(m)))
+def test_block_mask_pins_catch(mutant):
+    with pytest.raises((AssertionError, IndexError, ValueError)):
+        mask_pins(_mask_mutant(**mutant))
