@@ -338,6 +338,30 @@ def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
     torch.cuda.synchronize()
     attn_mean = statistics.mean(a.elapsed_time(b) for a, b in es)
     achieved = flops / (attn_mean * 1e-3) / 1e12
+    mask_path = None
+    if args.variant == "sparse":
+        # the same blocks as a bit mask: list building on the device + the same attention
+        nkb = -(-wl.N // KB)
+        mask = np.zeros(count.shape + (nkb,), dtype=bool)
+        for ix in np.ndindex(count.shape):
+            mask[ix][blocks[ix][:count[ix]]] = True
+        words = torch.from_numpy(wlmod.block_mask_words(mask).view(np.int32)).cuda()
+        wsm = va.block_mask_workspace_for(q, True)
+        va.prepare(k, v, workspace=wsm, stream=stream, **rope)
+        om = torch.empty_like(q)
+        call_m = lambda: va.attend_block_mask(q, wsm, words, scale=wl.scale, out=om, stream=stream, **rope)
+        call_m()
+        torch.cuda.synchronize()
+        es_m = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in es_m:
+            a.record(stream)
+            call_m()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms_m = statistics.mean(a.elapsed_time(b) for a, b in es_m)
+        mask_path = {"attend_block_mask_ms": round(ms_m, 3), "tflops": round(flops / (ms_m * 1e-3) / 1e12, 2),
+                     "bitwise_equal_to_lists": bool(torch.equal(om.view(torch.int16), o.view(torch.int16)))}
+        del wsm
     result = {
         "metric": METRIC, "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
@@ -347,6 +371,8 @@ def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
         "roofline": {"kernel": KERNEL, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
     }
+    if mask_path is not None:
+        result["bit_mask_path"] = mask_path
     if not args.no_parity:
         from threadpoolctl import threadpool_limits
         dec = oracle.decode_bf16

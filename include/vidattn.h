@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define VIDATTN_ABI_VERSION 4
+#define VIDATTN_ABI_VERSION 5
 
 typedef enum {
   VIDATTN_OK = 0,
@@ -246,6 +246,34 @@ typedef struct {
   int64_t F, H, W;
   int32_t r_f, r_h, r_w;
 } vidattn_window_desc;
+
+/* Block-sparse attention driven by a bit mask, the form of ScalingAttention's
+ * bit-wise block-sparse kernel (a per-head block mask; its abstract on the
+ * paper listing thelatestinai.com/papers/2606.17566): query block i (tokens
+ * 256i .. 256i+255) of each (b, head) attends only to the key blocks (64
+ * tokens each) whose bit is set. Same results as vidattn_fwd_attend_block_
+ * sparse given the set bits as ascending lists (bit for bit).
+ *   mask       uint32 [B][heads][ceil(N/256)][ceil(ceil(N/64)/32)], device
+ *              memory, 4-byte aligned: bit j%32 of word j/32 is key block j;
+ *              bits at or past ceil(N/64) are ignored. Must not overlap the
+ *              workspace.
+ *   workspace  the prepared key/value image (vidattn_fwd_prepare) in its
+ *              first vidattn_fwd_workspace_size bytes, and room after it for
+ *              the lists built from the mask: at least
+ *              vidattn_fwd_block_mask_workspace_size(...) bytes in all.
+ *   q, o       [B][heads][N][d] BF16; o must not overlap q or the workspace.
+ * A query block with no bit set gets O = 0. Only BF16 is implemented (F32:
+ * UNSUPPORTED). Other arguments as for vidattn_fwd_attend. */
+vidattn_status vidattn_fwd_attend_block_mask(const void* q, const uint32_t* mask, void* workspace, void* o,
+                                             vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                             float softmax_scale, const vidattn_rope3d_desc* rope,
+                                             size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes vidattn_fwd_attend_block_mask needs: vidattn_fwd_workspace_size
+ * plus the lists, 4*B*heads*ceil(N/256)*ceil(N/64) bytes and a 256-byte-padded
+ * count array. 0 for arguments it would reject by dtype or size. */
+size_t vidattn_fwd_block_mask_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                             int use_rope);
 
 /* Local-window attention: vidattn_fwd with every query restricted to its
  * window, the windowed-attention primitive of the vidax summary

@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_strings():
-    assert va.vidattn_abi_version() == 4
+    assert va.vidattn_abi_version() == 5
     for s, txt in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "workspace too small"),
                    (4, "HIP error")]:
         assert va.vidattn_status_string(s) == txt
@@ -199,6 +199,38 @@ def test_attend_block_sparse_rejects():
     assert bs(workspace_bytes=wsb - 1) == 3
     assert bs(d=96) == 2
     assert bs(o=QF) == 1 and "overlaps q" in va.vidattn_last_error()
+
+
+def test_attend_block_mask_rejects_and_sizes():
+    base = va.vidattn_fwd_workspace_size(va.BF16, 2, 40, N5, 128, True)
+    need = va.vidattn_fwd_block_mask_workspace_size(va.BF16, 2, 40, N5, 128, True)
+    nqb, nkt = -(-N5 // 256), -(-N5 // 64)
+    assert need == base + (80 * nqb * 4 + 255) // 256 * 256 + 80 * nqb * nkt * 4
+    assert va.vidattn_fwd_block_mask_workspace_size(va.F32, 2, 40, N5, 128, True) == 0
+    assert va.vidattn_fwd_block_mask_workspace_size(va.BF16, 2, 40, N5, 96, True) == 0
+    MK = 6 << 40  # fake mask address, far from the other fake buffers
+
+    def bm(mask=MK, dt=va.BF16, wsb=need, o=OF, ws=WSF):
+        return va.vidattn_fwd_attend_block_mask(QF, mask, ws, o, dt, 2, 40, N5, 128, 0.088, GOOD, wsb, None)
+    assert bm(mask=None) == 1 and "mask" in va.vidattn_last_error()
+    assert bm(mask=MK + 2) == 1 and "aligned" in va.vidattn_last_error()
+    assert bm(dt=va.F32) == 2
+    assert bm(wsb=need - 1) == 3
+    assert bm(wsb=base) == 3
+    assert bm(mask=WSF + need - 64) == 1 and "overlaps the workspace" in va.vidattn_last_error()
+    assert bm(o=WSF + 4096) == 1 and "overlap" in va.vidattn_last_error()
+
+
+def test_block_mask_words_layout():
+    """Bit j % 32 of word j // 32 is key block j; padding bits stay 0."""
+    import workloads as wlmod
+    import numpy as np
+    m = np.zeros((2, 3, 40), dtype=bool)
+    m[0, 0, 0] = m[0, 0, 31] = m[0, 0, 32] = m[1, 2, 39] = True
+    w = wlmod.block_mask_words(m)
+    assert w.shape == (2, 3, 2) and w.dtype == np.uint32
+    assert w[0, 0, 0] == (1 | (1 << 31)) and w[0, 0, 1] == 1 and w[1, 2, 1] == 1 << 7
+    assert int(w.sum()) - int(w[0, 0].sum()) - int(w[1, 2].sum()) == 0
 
 
 def test_window_rejects_and_sizes():

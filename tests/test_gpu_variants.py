@@ -210,6 +210,102 @@ def test_sparse_small(va, case, rope):
     assert _within(st), st
 
 
+# ------------------------------------------------------------------ block sparse from a bit mask
+
+def _random_mask(wl, seed, density, empty_every=0):
+    g = np.random.default_rng(seed)
+    nqb, nkb = -(-wl.N // QB), -(-wl.N // KB)
+    m = g.random((wl.B, wl.heads, nqb, nkb)) < density
+    m[..., nkb - 1] |= g.random((wl.B, wl.heads, nqb)) < 0.5  # the ragged last key block often set
+    if empty_every:
+        flat = m.reshape(-1, nkb)
+        flat[::empty_every] = False
+    return m
+
+
+def _check_mask(va, wl, host, mask, rope=True, rows=None, slices=None):
+    q, k, v = (parity.to_torch(host[n]) for n in ("q", "k", "v"))
+    kw = dict(grid=wl.grid, split=wl.split, theta=wl.theta) if rope else {}
+    ws = va.block_mask_workspace_for(q, rope)
+    va.prepare(k, v, workspace=ws, **kw)
+    words = torch.from_numpy(wlmod.block_mask_words(mask).view(np.int32)).cuda()
+    o = va.attend_block_mask(q, ws, words, scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    parts = []
+    for (b, h) in (slices or [(b, h) for b in range(wl.B) for h in range(wl.heads)]):
+        r = np.arange(wl.N) if rows is None else rows
+        got = parity.from_torch(o[b, h, torch.from_numpy(r).cuda()])
+        qd, kd, vd = (parity.decode(wl, host[n][b, h]) for n in ("q", "k", "v"))
+        ref = oracle.block_mask_attention(qd, kd, vd, wl.grid if rope else None, wl.split, wl.theta, wl.scale,
+                                          mask[b, h], QB, KB, rows=r)
+        empty = ~mask[b, h].any(axis=1)[r // QB]
+        assert np.all(got[empty] == 0.0)
+        parts.append(_stats(got, ref))
+    return o, ws, _merge(parts)
+
+
+MASK_CASES = [
+    # grid, d, split, B, H, bit density, every n-th mask row empty (0: none)
+    ((3, 11, 17), 128, (44, 42, 42), 2, 2, 0.3, 0),
+    ((3, 11, 17), 64, (16, 24, 24), 1, 3, 0.6, 3),
+    ((5, 13, 17), 128, (44, 42, 42), 1, 2, 0.15, 4),
+    ((2, 45, 80), 128, (44, 42, 42), 1, 1, 0.1, 5),  # 113 key blocks: four mask words per row
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: f"{c[0][0]}x{c[0][1]}x{c[0][2]}-d{c[1]}-p{c[5]}")
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
+def test_block_mask_small(va, case, rope):
+    grid, d, split, B, H, density, empty_every = case
+    wl = wlmod.custom(B, H, grid, d, split, seed_id=760 + d)
+    host = parity.host_inputs(wl)
+    mask = _random_mask(wl, seed=int(density * 100) + d, density=density, empty_every=empty_every)
+    _log(f"block mask {wl.name} density={density} rope={rope}")
+    _, _, st = _check_mask(va, wl, host, mask, rope)
+    _log(f"  {st}")
+    assert _within(st), st
+
+
+def test_block_mask_equals_the_lists_bitwise(va):
+    """The mask path and the list path on the same blocks give the same bits;
+    a full mask gives the dense attention's bits."""
+    wl = wlmod.custom(2, 2, (4, 15, 29), 128, (44, 42, 42), seed_id=770)
+    host = parity.host_inputs(wl)
+    mask = _random_mask(wl, seed=771, density=0.35, empty_every=4)
+    o_mask, ws, st = _check_mask(va, wl, host, mask)
+    assert _within(st), st
+    nkb = mask.shape[-1]
+    blocks = np.full(mask.shape, -1, dtype=np.int32)
+    count = mask.sum(axis=-1).astype(np.int32)
+    for idx in np.ndindex(mask.shape[:-1]):
+        sel = np.nonzero(mask[idx])[0]
+        blocks[idx][:len(sel)] = sel
+    q = parity.to_torch(host["q"])
+    kw = dict(grid=wl.grid, split=wl.split, theta=wl.theta)
+    o_list = va.attend_block_sparse(q, ws, torch.from_numpy(blocks).cuda(), torch.from_numpy(count).cuda(),
+                                    scale=wl.scale, **kw)
+    full = torch.from_numpy(wlmod.block_mask_words(np.ones_like(mask)).view(np.int32)).cuda()
+    o_full = va.attend_block_mask(q, ws, full, scale=wl.scale, **kw)
+    o_dense = va.attend(q, parity.to_torch(host["k"]), parity.to_torch(host["v"]), ws, scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_mask.view(torch.int16), o_list.view(torch.int16))
+    assert torch.equal(o_full.view(torch.int16), o_dense.view(torch.int16))
+    assert nkb == -(-wl.N // KB)
+
+
+def test_block_mask_large(va):
+    """The 32760-token grid (21 x 30 x 52), a 25 % mask, 256 sampled rows of
+    two slices."""
+    wl = wlmod.WORKLOADS[2]
+    host = parity.host_inputs(wl)
+    mask = _random_mask(wl, seed=780, density=0.25)
+    rows = wlmod.sample_rows(wl, 0, 0)
+    _log(f"block mask {wl.name} density=0.25")
+    _, _, st = _check_mask(va, wl, host, mask, rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)])
+    _log(f"  {st}")
+    assert _within(st), st
+
+
 def test_sparse_window_and_global_blocks(va):
     """Lists of the kind the pages describe (a local band around the query
     block plus a persistent global set), on a grid of 7 query blocks."""

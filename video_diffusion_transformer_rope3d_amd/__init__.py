@@ -20,11 +20,13 @@ __all__ = [
     "vidattn_last_error", "vidattn_abi_version", "attention", "prepare", "attend", "attend_subset",
     "attend_block_sparse", "rope3d", "workspace_for", "SPARSE_Q_BLOCK", "SPARSE_K_BLOCK", "EXPORTED_SYMBOLS",
     "WindowDesc", "vidattn_fwd_window", "vidattn_fwd_window_workspace_size", "window_attention",
+    "vidattn_fwd_attend_block_mask", "vidattn_fwd_block_mask_workspace_size", "attend_block_mask",
+    "block_mask_workspace_for",
 ]
 
 BF16, F16, F32 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 SPARSE_Q_BLOCK, SPARSE_K_BLOCK = 256, 64  # VIDATTN_SPARSE_Q_BLOCK, VIDATTN_SPARSE_K_BLOCK
 
@@ -32,7 +34,8 @@ EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_rope3d_tokens", "vidattn_fwd", "v
                     "vidattn_fwd_attend",
                     "vidattn_fwd_attend_subset", "vidattn_fwd_attend_block_sparse", "vidattn_fwd_window",
                     "vidattn_fwd_window_workspace_size", "vidattn_fwd_workspace_size", "vidattn_status_string",
-                    "vidattn_last_error", "vidattn_abi_version")
+                    "vidattn_last_error", "vidattn_abi_version", "vidattn_fwd_attend_block_mask",
+                    "vidattn_fwd_block_mask_workspace_size")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -134,6 +137,11 @@ def load() -> ctypes.CDLL:
     lib.vidattn_fwd_attend_block_sparse.restype = ctypes.c_int
     lib.vidattn_fwd_attend_block_sparse.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                                     ctypes.POINTER(Rope3dDesc), vp, vp, i64, sz, vp]
+    lib.vidattn_fwd_attend_block_mask.restype = ctypes.c_int
+    lib.vidattn_fwd_attend_block_mask.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
+                                                  ctypes.POINTER(Rope3dDesc), sz, vp]
+    lib.vidattn_fwd_block_mask_workspace_size.restype = sz
+    lib.vidattn_fwd_block_mask_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
     lib.vidattn_fwd_window.restype = ctypes.c_int
     lib.vidattn_fwd_window.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                        ctypes.POINTER(Rope3dDesc), ctypes.POINTER(WindowDesc), vp, sz, vp]
@@ -200,6 +208,17 @@ def vidattn_fwd_attend_block_sparse(q, workspace, o, dt, B, heads, N, d, softmax
     return load().vidattn_fwd_attend_block_sparse(q, workspace, o, dt, B, heads, N, d, softmax_scale,
                                                   ctypes.byref(rope) if rope is not None else None, kv_blocks,
                                                   kv_count, max_blocks, workspace_bytes, stream)
+
+
+def vidattn_fwd_attend_block_mask(q, mask, workspace, o, dt, B, heads, N, d, softmax_scale, rope, workspace_bytes,
+                                  stream=None) -> int:
+    return load().vidattn_fwd_attend_block_mask(q, mask, workspace, o, dt, B, heads, N, d, softmax_scale,
+                                                ctypes.byref(rope) if rope is not None else None, workspace_bytes,
+                                                stream)
+
+
+def vidattn_fwd_block_mask_workspace_size(dt, B, heads, N, d, use_rope) -> int:
+    return load().vidattn_fwd_block_mask_workspace_size(dt, B, heads, N, d, int(bool(use_rope)))
 
 
 def vidattn_fwd_window(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, window, workspace, workspace_bytes,
@@ -371,6 +390,39 @@ def attend_block_sparse(q, workspace, kv_blocks, kv_count, *, scale=None, grid=N
     _raise(vidattn_fwd_attend_block_sparse(q.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s, rope,
                                            kv_blocks.data_ptr(), kv_count.data_ptr(), kv_blocks.shape[3], nbytes,
                                            _stream(stream)))
+    return out
+
+
+def block_mask_workspace_for(q, use_rope: bool):
+    """A torch byte buffer large enough for prepare + attend_block_mask."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    n = vidattn_fwd_block_mask_workspace_size(_dt(q), B, H, N, d, use_rope)
+    if n == 0:
+        raise ValueError("block-mask attention supports bf16 [B, heads, N, d] with d in {64, 128}")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def attend_block_mask(q, workspace, mask, *, scale=None, grid=None, split=None, theta=10000.0, out=None,
+                      stream=None):
+    """Block-sparse attention from a bit mask: query block i (tokens
+    256i..256i+255) of each (b, head) attends only to the key blocks (64
+    tokens each) whose bit is set in ``mask``, an int32 device tensor of
+    packed words [B, heads, ceil(N/256), ceil(ceil(N/64)/32)] (bit j%32 of
+    word j//32 is key block j). ``workspace`` holds the prepared key/value
+    image (``prepare``) and room for the lists (``block_mask_workspace_for``)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    nqb, nkb = -(-N // SPARSE_Q_BLOCK), -(-N // SPARSE_K_BLOCK)
+    if mask.dtype != torch.int32 or tuple(mask.shape) != (B, H, nqb, -(-nkb // 32)) or not mask.is_contiguous():
+        raise ValueError(f"mask must be a contiguous int32 [{B}, {H}, {nqb}, {-(-nkb // 32)}] tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
+    ptr, nbytes = _ws(workspace)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _raise(vidattn_fwd_attend_block_mask(q.data_ptr(), mask.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s,
+                                         rope, nbytes, _stream(stream)))
     return out
 
 

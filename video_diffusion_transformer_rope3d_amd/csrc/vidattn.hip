@@ -13,6 +13,7 @@
 #include "attn_f32.hpp"
 #include "rope_kernels.hpp"
 #include "window_plan.hpp"
+#include "block_mask.hpp"
 
 using namespace vidattn;
 
@@ -502,6 +503,14 @@ vidattn_status vidattn_fwd_attend_block_sparse(const void* q, const void* worksp
 // Workspace of the local-window attention: the key/value image, then the
 // per-query-block tile counts (padded to 256 bytes), then the tile lists
 // (ceil(N/256) rows of ceil(N/64) entries).
+// Tile lists built from a block bit mask, in the workspace tail after the
+// prepared key/value image: counts [B*heads*nqb] (256-byte padded), then
+// lists [B*heads*nqb][nkt].
+static size_t block_mask_list_bytes(int64_t nbh, int64_t N) {
+  const int64_t nqb = (N + kBR - 1) / kBR, nkt = (N + kKT - 1) / kKT;
+  return (size_t)((nbh * nqb * 4 + 255) / 256 * 256 + nbh * nqb * nkt * 4);
+}
+
 static size_t window_plan_bytes(int64_t N) {
   const int64_t nqb = (N + kBR - 1) / kBR, nkt = (N + kKT - 1) / kKT;
   return (size_t)((nqb * 4 + 255) / 256 * 256 + nqb * nkt * 4);
@@ -567,6 +576,55 @@ vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, v
   x.wp = WindowParams{(int)window->F, (int)window->H, (int)window->W, rf, rh, rw, mode,
                       (float)(1.0 / (double)window->W), (float)(1.0 / (double)window->H)};
   if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, B * heads, N, d, softmax_scale, rp, st, x)) return s;
+  return ok();
+}
+
+size_t vidattn_fwd_block_mask_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                             int use_rope) {
+  if (dt != VIDATTN_BF16) return 0;
+  const size_t base = vidattn_fwd_workspace_size(dt, B, heads, N, d, use_rope);
+  return base ? base + block_mask_list_bytes(B * heads, N) : 0;
+}
+
+vidattn_status vidattn_fwd_attend_block_mask(const void* q, const uint32_t* mask, void* workspace, void* o,
+                                             vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
+                                             float softmax_scale, const vidattn_rope3d_desc* rope,
+                                             size_t workspace_bytes, void* hip_stream) {
+  if (dt != VIDATTN_BF16)
+    return fail(dt == VIDATTN_F32 || dt == VIDATTN_F16 ? VIDATTN_ERR_UNSUPPORTED : VIDATTN_ERR_INVALID_ARG,
+                "block-sparse attention is implemented for BF16");
+  if (!mask || (reinterpret_cast<uintptr_t>(mask) & 3u) != 0)
+    return fail(VIDATTN_ERR_INVALID_ARG, "mask must be non-null and 4-byte aligned");
+  const size_t lists = N >= 1 && N <= kMaxN && B >= 1 && heads >= 1 && B <= kMaxBH && heads <= kMaxBH &&
+                               B * heads <= kMaxBH
+                           ? block_mask_list_bytes(B * heads, N)
+                           : 0;
+  if (vidattn_status s = validate_fwd(Phase::kAttend, q, q, q, o, dt, B, heads, N, d, softmax_scale, rope, workspace,
+                                      workspace_bytes, -1, lists))
+    return s;
+  const int64_t nbh = B * heads, nqb = (N + kBR - 1) / kBR, nkt = (N + kKT - 1) / kKT;
+  const int64_t rows = nbh * nqb;
+  const int words = (int)((nkt + 31) / 32);
+  {  // the lists are written into the workspace while the mask is read
+    const char* mb = reinterpret_cast<const char*>(mask);
+    const char* wb = static_cast<const char*>(workspace);
+    const int64_t mask_bytes = rows * words * 4;
+    const int64_t ws_bytes = (int64_t)vidattn_fwd_block_mask_workspace_size(dt, B, heads, N, d, rope != nullptr);
+    if (mb < wb + ws_bytes && wb < mb + mask_bytes) return fail(VIDATTN_ERR_INVALID_ARG, "mask overlaps the workspace");
+  }
+  uint8_t* tail = static_cast<uint8_t*>(workspace) + vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
+  int32_t* kvc = reinterpret_cast<int32_t*>(tail);
+  int32_t* kvb = reinterpret_cast<int32_t*>(tail + (rows * 4 + 255) / 256 * 256);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipLaunchKernelGGL(block_mask_lists_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, mask, kvb, kvc,
+                     rows, words, (int)nkt);
+  if (vidattn_status s = hip_check("block mask lists launch")) return s;
+  const RopeParams rp = make_rope(rope);
+  AttendExtras x;
+  x.kvb = kvb;
+  x.kvc = kvc;
+  x.maxb = (int)nkt;
+  if (vidattn_status s = launch_attend(q, q, q, workspace, o, dt, nbh, N, d, softmax_scale, rp, st, x)) return s;
   return ok();
 }
 

@@ -241,3 +241,17 @@ def block_lists(wl: Workload, q_block: int, k_block: int, window: int, n_global:
         blocks[r, :len(x)] = x
         count[r] = len(x)
     return blocks.reshape(wl.B, wl.heads, nqb, width), count.reshape(wl.B, wl.heads, nqb)
+
+
+def block_mask_words(mask) -> np.ndarray:
+    """Pack a boolean key-block mask [..., n_query_blocks, n_key_blocks] into
+    uint32 words [..., n_query_blocks, ceil(n_key_blocks / 32)]: bit j % 32
+    of word j // 32 is key block j (the layout the bit-mask attention reads)."""
+    m = np.asarray(mask, dtype=bool)
+    nkb = m.shape[-1]
+    words = -(-nkb // 32)
+    padded = np.zeros(m.shape[:-1] + (words * 32,), dtype=bool)
+    padded[..., :nkb] = m
+    bits = padded.reshape(m.shape[:-1] + (words, 32)).astype(np.uint64) << np.arange(32, dtype=np.uint64)
+    return bits.sum(axis=-1).astype(np.uint32)
+
