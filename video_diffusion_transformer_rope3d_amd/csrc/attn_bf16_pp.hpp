@@ -20,9 +20,10 @@
 //   A       G_0 S_0    G_1 S_1       G_2 S_2           G_T
 //   B       G_0        S_0 G_1       S_1 G_2           S_T-1 G_T
 // (G_T is the last P.V alone.) Stage s of the ring holds K_j and V_{j-1} for
-// j = s mod NS and is read in period j only; group A refills the stage of
-// tile j-1 with tile j+NS-1 during its GEMM of period j, spreading the
-// direct-to-LDS loads between MFMA batches.
+// j = s mod NS and is read in period j only. In period j every wave issues
+// its share of the direct-to-LDS loads that refill the stage of tile j-1
+// with tile j+NS-1, at the start of its softmax phase (with
+// VIDATTN_BF16_FILL_IN_S = 0: between the MFMA batches of its GEMM phase).
 //
 // Numerics: the transposed products put all
 // scores and outputs of query q in lanes q and q+32, the running maximum m
