@@ -151,8 +151,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     uint8_t* st = lds + (j % NS) * STAGE;
     const uint8_t* src = blk < KBLK ? wsbh + (int64_t)tile_at(j) * STAGE + blk * 1024
                                     : wsbh + (int64_t)tile_at(j - 1) * STAGE + TILE + (blk - KBLK) * 1024;
-    __builtin_amdgcn_global_load_lds(src + lane * 16, (__attribute__((address_space(3))) void*)(st + blk * 1024), 16,
-                                     0, 0);
+    lds_dma16(src, (uint32_t)lane * 16u,
+              (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(st + blk * 1024));
   };
   auto issue = [&](int j) __attribute__((always_inline)) {
 #pragma unroll

@@ -91,6 +91,19 @@ __device__ __forceinline__ float xor32_sum(float v) {
 // and lgkmcnt(0) retires this wave's LDS reads before others may refill.
 // (The wait is the builtin, not inline asm, so the compiler's wait-count
 // tracking knows every LDS/scalar load has retired here.)
+// Direct global -> LDS copy of 16 bytes per lane: lane i reads base + voff
+// (base uniform, in SGPRs; voff per lane) and the data lands at LDS byte
+// address lds + 16 i. Written as inline assembly so that the compiler does
+// not track it: with a compiler-tracked LDS DMA in flight, every LDS read
+// wait in the same loop becomes lgkmcnt(0), which drains the operand
+// double buffer at every other MFMA batch. The caller orders these copies
+// with explicit vmcnt waits and barriers. (m0 holds the LDS address; the
+// nop covers the m0 write before the LDS DMA.)
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ void lds_barrier() {
   constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);  // lgkmcnt(0), vmcnt/expcnt untouched
   asm volatile("" ::: "memory");
