@@ -144,19 +144,20 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // 0 .. STAGE/1024-1 of the stage; K first). Load r of wave w moves block
   // r*NW + w. At the ends (no V_{-1}, no K_nt) a neighbouring tile is copied
   // into the unused half so that every stage costs each loader wave exactly
-  // STAGE_LOADS loads (the vmcnt arithmetic below relies on it).
-  auto issue_one = [&](int j, int r) __attribute__((always_inline)) {
+  // STAGE_LOADS loads (the vmcnt arithmetic below relies on it). tk and tv
+  // are the workspace tiles of loop tiles j and j-1.
+  auto issue_one = [&](int j, int r, int tk, int tv) __attribute__((always_inline)) {
     constexpr int KBLK = TILE / 1024;
     const int blk = r * NLOADER + wave;
     uint8_t* st = lds + (j % NS) * STAGE;
-    const uint8_t* src = blk < KBLK ? wsbh + (int64_t)tile_at(j) * STAGE + blk * 1024
-                                    : wsbh + (int64_t)tile_at(j - 1) * STAGE + TILE + (blk - KBLK) * 1024;
+    const uint8_t* src = blk < KBLK ? wsbh + (int64_t)tk * STAGE + blk * 1024
+                                    : wsbh + (int64_t)tv * STAGE + TILE + (blk - KBLK) * 1024;
     lds_dma16(src, (uint32_t)lane * 16u,
               (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(st + blk * 1024));
   };
-  auto issue = [&](int j) __attribute__((always_inline)) {
+  auto issue = [&](int j, int tk, int tv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < STAGE_LOADS; ++r) issue_one(j, r);
+    for (int r = 0; r < STAGE_LOADS; ++r) issue_one(j, r, tk, tv);
   };
 
   // ---- queries: rotate, pre-scale by scale*log2(e), round to fp16 (B operand).
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       pos = t < 0 ? 0 : (t < N ? t : N - 1);
     }
     for (int j = 0; j < NS - 1; ++j)
-      if (j <= nt) issue(j);
+      if (j <= nt) issue(j, tile_at(j), tile_at(j - 1));
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       float x[8];
@@ -268,15 +269,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     lds_barrier();
   };
 
-  // Window variant: bit 8(2kb + h) + e of window_vis(jj) is set when this
-  // lane's key 32kb + 16h + 8g + e of tile jj lies inside its query's box.
+  // Window variant: bit 8(2kb + h) + e of window_vis(t) is set when this
+  // lane's key 32kb + 16h + 8g + e of workspace tile t lies inside its query's box.
   // It depends on the tile and the query only, so the GEMM phase folds it
   // into the accumulator input of the first score MFMA (-m, or -inf for a
   // key outside the box) while the matrix core runs the P.V products.
-  auto window_vis = [&](int jj) __attribute__((always_inline)) {
+  auto window_vis = [&](int tile) __attribute__((always_inline)) {
     unsigned vis = 0;
     if constexpr (WIN) {
-      const int base = tile_at(jj) * KT;
+      const int base = tile * KT;
       const unsigned fspan = 2u * wp.rf, yspan = 2u * wp.rh, xspan = 2u * wp.rw;
       const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
       if (wp.mode == 2) {
@@ -356,6 +357,26 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // outside the window variant
   unsigned wvis = ~0u;
 
+  // Workspace tiles of loop tiles j-1 .. j+NS-1 in tile period j:
+  // tw[k] = tile_at(j - 1 + k). Each period reads one list entry, for the
+  // next period, in a softmax phase: the list reads are scalar loads, and
+  // one in flight during a GEMM phase would turn every LDS operand wait
+  // there into a full drain.
+  // (Dense: tile_at is the clamped loop index and tw is not used.)
+  int tw[NS + 1];
+#pragma unroll
+  for (int k = 0; k <= NS; ++k) tw[k] = SPARSE ? tile_at(k - 1) : 0;
+  int tnext = 0;  // tile_at(i + NS), read in period i
+  auto advance = [&]() __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) tw[k] = tw[k + 1];
+      tw[NS] = tnext;
+    }
+  };
+  // workspace tile of loop tile j - 1 + k in period j
+  auto tile_k = [&](int k, int j) __attribute__((always_inline)) { return SPARSE ? tw[k] : tile_at(j - 1 + k); };
+
   // GEMM phase of tile jj: O^T += V_{jj-1}^T P^T (PV), S'^T = K_jj Q'^T - m (SC).
   // The operands (16 B per lane each) stream from LDS in batches of RB,
   // double-buffered in registers: batch b+1 is read while the MFMAs of
@@ -378,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     // for a key outside the window (sign-extended bit, then a bit select)
     f32x16 cneg[2];
     if constexpr (WIN && decltype(SC)::value) {
-      const unsigned vis = window_vis(jj);
+      const unsigned vis = window_vis(tw[1]);
       wvis = vis;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -403,7 +424,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       if constexpr (decltype(FILL)::value) {
         constexpr int NB = NOP / RB;
 #pragma unroll
-        for (int r = b * STAGE_LOADS / NB; r < (b + 1) * STAGE_LOADS / NB; ++r) issue_one(fill, r);
+        for (int r = b * STAGE_LOADS / NB; r < (b + 1) * STAGE_LOADS / NB; ++r) issue_one(fill, r, tile_k(NS, jj), tile_k(NS - 1, jj));
       }
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
@@ -429,10 +450,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
   };
 
-  // SOFTMAX phase of tile jj (in the last tile, keys past N get -inf).
-  auto softmax = [&](int jj) __attribute__((always_inline)) {
+  // SOFTMAX phase of the scores of workspace tile t (in the last tile, keys
+  // past N get -inf).
+  auto softmax = [&](int t) __attribute__((always_inline)) {
     {
-      if (tail < KT && tile_at(jj) == nkt - 1) {
+      if (tail < KT && t == nkt - 1) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -491,52 +513,85 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // MFMA batches of its GEMM phase.
   constexpr bool kFillInS = VIDATTN_BF16_FILL_IN_S != 0;
   using FG = std::integral_constant<bool, !kFillInS>;  // GEMM carries the refill
-  auto sm = [&](auto FILL, int j, int fill_tile) __attribute__((always_inline)) {
-    if constexpr (kFillInS && decltype(FILL)::value) issue(fill_tile);
-    softmax(j);
+  // Softmax phase of workspace tile t in period i: the refill share of
+  // tile fill_tile (FILL_IN_S), the list read for period i + 1, then the
+  // softmax itself, during which the read lands. The scheduling barriers
+  // keep the list read out of the GEMM phase before (group A) and the
+  // refill ahead of the softmax arithmetic (group B, GRB, whose softmax
+  // opens the period).
+  auto prefetch = [&](int i) __attribute__((always_inline)) {
+    if constexpr (SPARSE) tnext = tile_at(i + NS);
+  };
+  auto sm = [&](auto FILL, auto GRB, int t, int fill_tile, int i) __attribute__((always_inline)) {
+    if constexpr (SPARSE) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kFillInS && decltype(FILL)::value) issue(fill_tile, tile_k(NS, i), tile_k(NS - 1, i));
+    if constexpr (decltype(GRB)::value) __builtin_amdgcn_sched_barrier(0);
+    prefetch(i);
+    softmax(t);
+  };
+  // before a GEMM phase that no barrier precedes: no list read in flight
+  auto lists_landed = [&]() __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   tile_barrier(0);
   if (group == 0) {  // period i: GEMM_i then SOFTMAX_i
     if (NS - 1 <= nt) {
       gemm(F{}, T{}, FG{}, 0);
-      sm(T{}, 0, NS - 1);
+      sm(T{}, F{}, tile_k(1, 0), NS - 1, 0);
     } else {
       gemm(F{}, T{}, F{}, 0);
-      sm(F{}, 0, 0);
+      sm(F{}, F{}, tile_k(1, 0), 0, 0);
     }
     int j = 1;
     for (; j < nt && j + NS - 1 <= nt; ++j) {
+      advance();
       tile_barrier(j);
       gemm(T{}, T{}, FG{}, j);
-      sm(T{}, j, j + NS - 1);
+      sm(T{}, F{}, tile_k(1, j), j + NS - 1, j);
     }
     for (; j < nt; ++j) {
+      advance();
       tile_barrier(j);
       gemm(T{}, T{}, F{}, j);
-      sm(F{}, j, 0);
+      sm(F{}, F{}, tile_k(1, j), 0, j);
     }
     tile_barrier(nt);
     gemm(T{}, F{}, F{}, nt);
   } else {  // period i: SOFTMAX_{i-1} then GEMM_i (period 0: GEMM_0 only)
     if (NS - 1 <= nt) {
-      if constexpr (kFillInS) issue(NS - 1);
+      if constexpr (kFillInS) issue(NS - 1, tile_k(NS, 0), tile_k(NS - 1, 0));
+      __builtin_amdgcn_sched_barrier(0);
+      prefetch(0);
+      lists_landed();
       gemm(F{}, T{}, FG{}, 0);
     } else {
+      prefetch(0);
+      lists_landed();
       gemm(F{}, T{}, F{}, 0);
     }
     int j = 1;
     for (; j < nt && j + NS - 1 <= nt; ++j) {
+      advance();
       tile_barrier(j);
-      sm(T{}, j - 1, j + NS - 1);
+      sm(T{}, T{}, tile_k(0, j), j + NS - 1, j);
+      lists_landed();
       gemm(T{}, T{}, FG{}, j);
     }
     for (; j < nt; ++j) {
+      advance();
       tile_barrier(j);
-      sm(F{}, j - 1, 0);
+      sm(F{}, T{}, tile_k(0, j), 0, j);
+      lists_landed();
       gemm(T{}, T{}, F{}, j);
     }
+    advance();
     tile_barrier(nt);
-    sm(F{}, nt - 1, 0);
+    softmax(tile_k(0, nt));
     gemm(T{}, F{}, F{}, nt);
   }
 

@@ -106,10 +106,14 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
 
 __device__ __forceinline__ void lds_barrier() {
   constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);  // lgkmcnt(0), vmcnt/expcnt untouched
+  // The scheduling barriers keep arithmetic on its side of the workgroup
+  // barrier too (the s_barrier alone fences only memory operations).
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(kLgkm0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Row index permutation of a 32-row MFMA operand block: swaps bits 2 and 3.
