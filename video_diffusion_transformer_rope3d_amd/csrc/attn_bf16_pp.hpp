@@ -177,6 +177,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     }
     for (int j = 0; j < NS - 1; ++j)
       if (j <= nt) issue(j, tile_at(j), tile_at(j - 1));
+    // grid coordinates of the row, once
+    const int hw = rp.H * rp.W;
+    const int cf = rp.enabled ? pos / hw : 0;
+    const int cy = rp.enabled ? (pos - cf * hw) / rp.W : 0;
+    const int cx = pos - cf * hw - cy * rp.W;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       float x[8];
@@ -184,8 +189,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       if (rp.enabled) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // pair 8s + 4g + j: both candidates (g = 0, 1) are wave-uniform
+          // kernel arguments, read once into scalar registers
+          const int p0 = 8 * s + j, p1 = p0 + 4;
+          const double w0 = uniform_f64(rp.omega[p0]), w1 = uniform_f64(rp.omega[p1]);
+          const int a0 = p0 < rp.pair_t ? cf : (p0 < rp.pair_th ? cy : cx);
+          const int a1 = p1 < rp.pair_t ? cf : (p1 < rp.pair_th ? cy : cx);
           float c, sn;
-          rope_cos_sin(rp, pos, 8 * s + 4 * g + j, c, sn);
+          rope_angle_cos_sin(g ? a1 : a0, g ? w1 : w0, c, sn);
           rotate_pair(x[2 * j], x[2 * j + 1], c, sn);
         }
       }

@@ -57,11 +57,24 @@ __device__ __forceinline__ int rope_pos(const RopeParams& rp, int n, int p) {
 // so the reduced value is exact to ~1e-11), rounded to fp32 in [-pi, pi],
 // and its cos/sin taken in fp32 (absolute error ~2e-7, far below the fp16 /
 // bf16 rounding of the rotated values and within the fp32 path's bounds).
-__device__ __forceinline__ void rope_cos_sin(const RopeParams& rp, int n, int p, float& c, float& s) {
-  const double ang = (double)rope_pos(rp, n, p) * rp.omega[p];
+__device__ __forceinline__ void rope_angle_cos_sin(int pos, double omega, float& c, float& s) {
+  const double ang = (double)pos * omega;
   const double turns = rint(ang * 0.15915494309189535);  // nearest multiple of 2*pi
   const float r = (float)fma(-turns, 6.283185307179586, ang);
   sincosf(r, &s, &c);
+}
+__device__ __forceinline__ void rope_cos_sin(const RopeParams& rp, int n, int p, float& c, float& s) {
+  rope_angle_cos_sin(rope_pos(rp, n, p), rp.omega[p], c, s);
+}
+
+// A wave-uniform double kept in scalar registers (its halves read from the
+// first lane), so that a per-lane choice between two of them stays a select
+// instead of becoming one per-lane load from a chosen address.
+__device__ __forceinline__ double uniform_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // Rotate one pair in fp32: (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
