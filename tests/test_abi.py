@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_strings():
-    assert va.vidattn_abi_version() == 5
+    assert va.vidattn_abi_version() == 5 == va.ABI_VERSION
     for s, txt in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "workspace too small"),
                    (4, "HIP error")]:
         assert va.vidattn_status_string(s) == txt
@@ -279,3 +279,17 @@ def test_library_imports_no_allocation_copy_or_sync():
                "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipGetErrorString", "hipGetLastError",
                "hipLaunchKernel"}
     assert set(hip) <= allowed, sorted(set(hip) - allowed)
+
+
+def test_build_entry_checks_the_binding_abi():
+    """The build entry point compares the library's ABI with the binding's
+    constant, not with a number of its own that could fall behind."""
+    import importlib.util
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "__graft_entry__.py")
+    spec = importlib.util.spec_from_file_location("_graft_entry_probe", path)
+    entry = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(entry)
+    import inspect
+    src = inspect.getsource(entry.build)
+    assert "va.ABI_VERSION" in src and "== 3" not in src
