@@ -112,6 +112,12 @@ SMALL = [
     ((3, 5, 7), 128, (44, 42, 42), "f32", 2, 1),      # fp32 d=128, ragged
     ((1, 1, 1), 64, (16, 24, 24), "f32", 1, 1),       # fp32 N = 1
     ((3, 7, 9), 64, (0, 32, 32), "f32", 1, 2),        # empty frame chunk
+    # uneven splits: the axis boundaries fall inside and between the
+    # 4-pair groups of the two lane halves in other places
+    ((3, 5, 7), 128, (2, 2, 124), "bf16", 1, 1),
+    ((3, 5, 7), 128, (124, 2, 2), "bf16", 1, 1),
+    ((3, 5, 7), 128, (6, 0, 122), "bf16", 1, 1),      # empty row chunk
+    ((2, 9, 11), 64, (0, 64, 0), "bf16", 1, 1),       # rows only
 ]
 
 
