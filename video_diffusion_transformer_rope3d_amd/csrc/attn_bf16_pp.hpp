@@ -22,8 +22,7 @@
 // (G_T is the last P.V alone.) Stage s of the ring holds K_j and V_{j-1} for
 // j = s mod NS and is read in period j only. In period j every wave issues
 // its share of the direct-to-LDS loads that refill the stage of tile j-1
-// with tile j+NS-1, at the start of its softmax phase (with
-// VIDATTN_BF16_FILL_IN_S = 0: between the MFMA batches of its GEMM phase).
+// with tile j+NS-1, at the start of its softmax phase.
 //
 // Numerics: the transposed products put all
 // scores and outputs of query q in lanes q and q+32, the running maximum m
@@ -48,11 +47,6 @@
 
 #include <type_traits>
 
-// Where each wave issues its share of the ring refill: 1 = at the start of
-// its softmax phase, 0 = between the MFMA batches of its GEMM phase.
-#ifndef VIDATTN_BF16_FILL_IN_S
-#define VIDATTN_BF16_FILL_IN_S 1
-#endif
 
 #include "common.hpp"
 
@@ -393,8 +387,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // double-buffered in registers: batch b+1 is read while the MFMAs of
   // batch b run, so each MFMA finds its operand already loaded.
   constexpr int RB = 4;
-  auto gemm = [&](auto PV, auto SC, auto FILL, int jj) __attribute__((always_inline)) {
-    const int fill = jj + NS - 1;  // tile loaded into the ring when FILL (period jj fills tile jj+NS-1)
+  auto gemm = [&](auto PV, auto SC, int jj) __attribute__((always_inline)) {
     // one register holds this lane's address in the stage; the operand
     // offsets (< 32 KB) then fit the ds_read immediate field
     uint32_t sb = (uint32_t)(uintptr_t)(lds + (jj % NS) * STAGE + lane * 16);
@@ -431,12 +424,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
 #pragma unroll
         for (int r = 0; r < RB; ++r) buf[(b + 1) & 1][r] = *reinterpret_cast<const u32x4*>(addr((b + 1) * RB + r));
       }
-      // the ring refill (group A only) rides in the MFMA shadow, spread over the batches
-      if constexpr (decltype(FILL)::value) {
-        constexpr int NB = NOP / RB;
-#pragma unroll
-        for (int r = b * STAGE_LOADS / NB; r < (b + 1) * STAGE_LOADS / NB; ++r) issue_one(fill, r, tile_k(NS, jj), tile_k(NS - 1, jj));
-      }
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const int i = b * RB + r;
@@ -456,7 +443,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     for (int b = 0; b < NOP / RB; ++b) {
       __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
       if (b > 0) __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, STAGE_LOADS, 0);  // VMEM read (ring refill), if any
     }
     __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
   };
@@ -514,18 +500,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   using F = std::false_type;
   // One barrier per tile period i; within it group A runs GEMM_i then
   // SOFTMAX_i and group B runs SOFTMAX_{i-1} then GEMM_i, so on every SIMD
-  // the matrix core and the vector ALU serve different waves. Group A refills
-  // the ring with tile i+NS-1 inside GEMM_i.
+  // the matrix core and the vector ALU serve different waves.
   //   A: [b0] G_0 S_0 [b1] G_1 S_1 ... [b(T-1)] G_T-1 S_T-1 [bT] G_T(P.V)
   //   B: [b0] G_0     [b1] S_0 G_1 ... [b(T-1)] S_T-2 G_T-1 [bT] S_T-1 G_T(P.V)
   // Period i refills the ring with tile i+NS-1 while that is <= nkt (the
-  // "refill" loops below; the "drain" loops follow). With FILL_IN_S each wave
-  // issues its share at the start of its softmax phase, otherwise between the
-  // MFMA batches of its GEMM phase.
-  constexpr bool kFillInS = VIDATTN_BF16_FILL_IN_S != 0;
-  using FG = std::integral_constant<bool, !kFillInS>;  // GEMM carries the refill
+  // "refill" loops below; the "drain" loops follow); each wave issues its
+  // share at the start of its softmax phase.
   // Softmax phase of workspace tile t in period i: the refill share of
-  // tile fill_tile (FILL_IN_S), the list read for period i + 1, then the
+  // tile fill_tile (FILL), the list read for period i + 1, then the
   // softmax itself, during which the read lands. The scheduling barriers
   // keep the list read out of the GEMM phase before (group A) and the
   // refill ahead of the softmax arithmetic (group B, GRB, whose softmax
@@ -535,7 +517,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   };
   auto sm = [&](auto FILL, auto GRB, int t, int fill_tile, int i) __attribute__((always_inline)) {
     if constexpr (SPARSE) __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kFillInS && decltype(FILL)::value) issue(fill_tile, tile_k(NS, i), tile_k(NS - 1, i));
+    if constexpr (decltype(FILL)::value) issue(fill_tile, tile_k(NS, i), tile_k(NS - 1, i));
     if constexpr (decltype(GRB)::value) __builtin_amdgcn_sched_barrier(0);
     prefetch(i);
     softmax(t);
@@ -552,38 +534,38 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   tile_barrier(0);
   if (group == 0) {  // period i: GEMM_i then SOFTMAX_i
     if (NS - 1 <= nt) {
-      gemm(F{}, T{}, FG{}, 0);
+      gemm(F{}, T{}, 0);
       sm(T{}, F{}, tile_k(1, 0), NS - 1, 0);
     } else {
-      gemm(F{}, T{}, F{}, 0);
+      gemm(F{}, T{}, 0);
       sm(F{}, F{}, tile_k(1, 0), 0, 0);
     }
     int j = 1;
     for (; j < nt && j + NS - 1 <= nt; ++j) {
       advance();
       tile_barrier(j);
-      gemm(T{}, T{}, FG{}, j);
+      gemm(T{}, T{}, j);
       sm(T{}, F{}, tile_k(1, j), j + NS - 1, j);
     }
     for (; j < nt; ++j) {
       advance();
       tile_barrier(j);
-      gemm(T{}, T{}, F{}, j);
+      gemm(T{}, T{}, j);
       sm(F{}, F{}, tile_k(1, j), 0, j);
     }
     tile_barrier(nt);
-    gemm(T{}, F{}, F{}, nt);
+    gemm(T{}, F{}, nt);
   } else {  // period i: SOFTMAX_{i-1} then GEMM_i (period 0: GEMM_0 only)
     if (NS - 1 <= nt) {
-      if constexpr (kFillInS) issue(NS - 1, tile_k(NS, 0), tile_k(NS - 1, 0));
+      issue(NS - 1, tile_k(NS, 0), tile_k(NS - 1, 0));
       __builtin_amdgcn_sched_barrier(0);
       prefetch(0);
       lists_landed();
-      gemm(F{}, T{}, FG{}, 0);
+      gemm(F{}, T{}, 0);
     } else {
       prefetch(0);
       lists_landed();
-      gemm(F{}, T{}, F{}, 0);
+      gemm(F{}, T{}, 0);
     }
     int j = 1;
     for (; j < nt && j + NS - 1 <= nt; ++j) {
@@ -591,19 +573,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       tile_barrier(j);
       sm(T{}, T{}, tile_k(0, j), j + NS - 1, j);
       lists_landed();
-      gemm(T{}, T{}, FG{}, j);
+      gemm(T{}, T{}, j);
     }
     for (; j < nt; ++j) {
       advance();
       tile_barrier(j);
       sm(F{}, T{}, tile_k(0, j), 0, j);
       lists_landed();
-      gemm(T{}, T{}, F{}, j);
+      gemm(T{}, T{}, j);
     }
     advance();
     tile_barrier(nt);
     softmax(tile_k(0, nt));
-    gemm(T{}, F{}, F{}, nt);
+    gemm(T{}, F{}, nt);
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16.
