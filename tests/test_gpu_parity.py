@@ -252,6 +252,21 @@ def test_single_token_gives_v(va):
     assert torch.equal(o.view(torch.int16), v.view(torch.int16))
 
 
+def test_many_slices_single_token(va):
+    """270000 (batch, head) slices of one token each: the pre-pass and the
+    rotation spread the slices over the grid's second dimension, which must
+    stay within 65535 blocks, and one key gives O = V exactly."""
+    B, H, d = 1, 270000, 64
+    _log(f"many slices B={B} heads={H} N=1 d={d}")
+    q, k, v = (_rand((B, H, 1, d), torch.bfloat16, 70 + i) for i in range(3))
+    o = va.attention(q, k, v, grid=(1, 1, 1), split=(16, 24, 24))
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), v.view(torch.int16))
+    r = va.rope3d(q, (1, 1, 1), (16, 24, 24), 1e4)
+    torch.cuda.synchronize()
+    assert torch.equal(r.view(torch.int16), q.view(torch.int16))  # position (0, 0, 0) is the identity
+
+
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_bitwise_deterministic_and_overwrites_poison(va, dt):
     shape = (2, 4, 1105, 128)

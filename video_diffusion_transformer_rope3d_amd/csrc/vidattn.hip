@@ -118,6 +118,8 @@ int bh_group(int64_t items_blocks, int64_t nbh) {
   // two or eight, 1.19 at sixteen and 1.44 at one).
   int g = 4;
   while (g > 1 && items_blocks * ((nbh + g - 1) / g) < 1024) g >>= 1;
+  // keep the grid's y extent within 65535 for any number of slices
+  while ((nbh + g - 1) / g > 65535) g <<= 1;
   return g;
 }
 
