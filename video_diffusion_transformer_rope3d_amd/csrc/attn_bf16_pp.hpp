@@ -20,9 +20,9 @@
 //   A       G_0 S_0    G_1 S_1       G_2 S_2           G_T
 //   B       G_0        S_0 G_1       S_1 G_2           S_T-1 G_T
 // (G_T is the last P.V alone.) Stage s of the ring holds K_j and V_{j-1} for
-// j = s mod NS and is read in period j only. In period j every wave issues
-// its share of the direct-to-LDS loads that refill the stage of tile j-1
-// with tile j+NS-1, at the start of its softmax phase.
+// j = s mod NS and is read in period j only. In period j the waves of group
+// A issue the direct-to-LDS loads that refill the stage of tile j-1 with
+// tile j+NS-1, at the start of their softmax phase.
 //
 // Numerics: the transposed products put all
 // scores and outputs of query q in lanes q and q+32, the running maximum m
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   constexpr int MS = KT / 16;     // 16-key steps of the P.V product
   constexpr int TILE = KT * D * 2;  // bytes of one K tile (and of one V tile)
   constexpr int STAGE = 2 * TILE;
-  constexpr int NLOADER = NW;                          // every wave takes a share of the ring refill
+  constexpr int NLOADER = NW / 2;                      // the waves of group A refill the ring
   constexpr int STAGE_LOADS = STAGE / (NLOADER * 1024);  // 1 KB loads per loader wave per stage
   static_assert(STAGE % (NLOADER * 1024) == 0, "stage must split into whole 1 KB wave loads");
   static_assert(NS >= 2 && STAGE_LOADS * (NS - 2) < 64, "vmcnt range");
@@ -135,8 +135,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   }
 
   // Fill the stage of loop tile j: K of tile j and V of tile j-1 (blocks
-  // 0 .. STAGE/1024-1 of the stage; K first). Load r of wave w moves block
-  // r*NW + w. At the ends (no V_{-1}, no K_nt) a neighbouring tile is copied
+  // 0 .. STAGE/1024-1 of the stage; K first). Load r of loader wave w (the
+  // waves of group A) moves block r*NLOADER + w. At the ends (no V_{-1}, no
+  // K_nt) a neighbouring tile is copied
   // into the unused half so that every stage costs each loader wave exactly
   // STAGE_LOADS loads (the vmcnt arithmetic below relies on it). tk and tv
   // are the workspace tiles of loop tiles j and j-1.
@@ -169,8 +170,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       const int t = qidx[pos];
       pos = t < 0 ? 0 : (t < N ? t : N - 1);
     }
-    for (int j = 0; j < NS - 1; ++j)
-      if (j <= nt) issue(j, tile_at(j), tile_at(j - 1));
+    if (group == 0)
+      for (int j = 0; j < NS - 1; ++j)
+        if (j <= nt) issue(j, tile_at(j), tile_at(j - 1));
     // grid coordinates of the row, once
     const int hw = rp.H * rp.W;
     const int cf = rp.enabled ? pos / hw : 0;
@@ -504,21 +506,20 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   //   A: [b0] G_0 S_0 [b1] G_1 S_1 ... [b(T-1)] G_T-1 S_T-1 [bT] G_T(P.V)
   //   B: [b0] G_0     [b1] S_0 G_1 ... [b(T-1)] S_T-2 G_T-1 [bT] S_T-1 G_T(P.V)
   // Period i refills the ring with tile i+NS-1 while that is <= nkt (the
-  // "refill" loops below; the "drain" loops follow); each wave issues its
-  // share at the start of its softmax phase.
-  // Softmax phase of workspace tile t in period i: the refill share of
-  // tile fill_tile (FILL), the list read for period i + 1, then the
-  // softmax itself, during which the read lands. The scheduling barriers
-  // keep the list read out of the GEMM phase before (group A) and the
-  // refill ahead of the softmax arithmetic (group B, GRB, whose softmax
-  // opens the period).
+  // "refill" loops below; the "drain" loops follow). The waves of group A
+  // issue it at the start of their softmax phase: group B's softmax runs
+  // beside group A's GEMM phase, gets few vector issue slots there and is
+  // the longer path through the period, so it carries none of the refill.
+  // Softmax phase of workspace tile t in period i: the refill of tile
+  // fill_tile (FILL), the list read for period i + 1, then the softmax
+  // itself, during which the read lands. The scheduling barrier keeps the
+  // list read out of the GEMM phase before.
   auto prefetch = [&](int i) __attribute__((always_inline)) {
     if constexpr (SPARSE) tnext = tile_at(i + NS);
   };
-  auto sm = [&](auto FILL, auto GRB, int t, int fill_tile, int i) __attribute__((always_inline)) {
+  auto sm = [&](auto FILL, int t, int fill_tile, int i) __attribute__((always_inline)) {
     if constexpr (SPARSE) __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(FILL)::value) issue(fill_tile, tile_k(NS, i), tile_k(NS - 1, i));
-    if constexpr (decltype(GRB)::value) __builtin_amdgcn_sched_barrier(0);
     prefetch(i);
     softmax(t);
   };
@@ -535,50 +536,34 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   if (group == 0) {  // period i: GEMM_i then SOFTMAX_i
     if (NS - 1 <= nt) {
       gemm(F{}, T{}, 0);
-      sm(T{}, F{}, tile_k(1, 0), NS - 1, 0);
+      sm(T{}, tile_k(1, 0), NS - 1, 0);
     } else {
       gemm(F{}, T{}, 0);
-      sm(F{}, F{}, tile_k(1, 0), 0, 0);
+      sm(F{}, tile_k(1, 0), 0, 0);
     }
     int j = 1;
     for (; j < nt && j + NS - 1 <= nt; ++j) {
       advance();
       tile_barrier(j);
       gemm(T{}, T{}, j);
-      sm(T{}, F{}, tile_k(1, j), j + NS - 1, j);
+      sm(T{}, tile_k(1, j), j + NS - 1, j);
     }
     for (; j < nt; ++j) {
       advance();
       tile_barrier(j);
       gemm(T{}, T{}, j);
-      sm(F{}, F{}, tile_k(1, j), 0, j);
+      sm(F{}, tile_k(1, j), 0, j);
     }
     tile_barrier(nt);
     gemm(T{}, F{}, nt);
   } else {  // period i: SOFTMAX_{i-1} then GEMM_i (period 0: GEMM_0 only)
-    if (NS - 1 <= nt) {
-      issue(NS - 1, tile_k(NS, 0), tile_k(NS - 1, 0));
-      __builtin_amdgcn_sched_barrier(0);
-      prefetch(0);
-      lists_landed();
-      gemm(F{}, T{}, 0);
-    } else {
-      prefetch(0);
-      lists_landed();
-      gemm(F{}, T{}, 0);
-    }
-    int j = 1;
-    for (; j < nt && j + NS - 1 <= nt; ++j) {
+    prefetch(0);
+    lists_landed();
+    gemm(F{}, T{}, 0);
+    for (int j = 1; j < nt; ++j) {
       advance();
       tile_barrier(j);
-      sm(T{}, T{}, tile_k(0, j), j + NS - 1, j);
-      lists_landed();
-      gemm(T{}, T{}, j);
-    }
-    for (; j < nt; ++j) {
-      advance();
-      tile_barrier(j);
-      sm(F{}, T{}, tile_k(0, j), 0, j);
+      sm(F{}, tile_k(0, j), 0, j);
       lists_landed();
       gemm(T{}, T{}, j);
     }
