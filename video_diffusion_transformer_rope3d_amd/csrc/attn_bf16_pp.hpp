@@ -22,7 +22,8 @@
 // (G_T is the last P.V alone.) Stage s of the ring holds K_j and V_{j-1} for
 // j = s mod NS and is read in period j only. In period j the waves of group
 // A issue the direct-to-LDS loads that refill the stage of tile j-1 with
-// tile j+NS-1, at the start of their softmax phase.
+// tile j+NS-1, at the start of their softmax phase (the sparse variants
+// split them with group B, which issues its share at the period start).
 //
 // Numerics: the transposed products put all
 // scores and outputs of query q in lanes q and q+32, the running maximum m
@@ -82,7 +83,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   constexpr int MS = KT / 16;     // 16-key steps of the P.V product
   constexpr int TILE = KT * D * 2;  // bytes of one K tile (and of one V tile)
   constexpr int STAGE = 2 * TILE;
-  constexpr int NLOADER = NW / 2;                      // the waves of group A refill the ring
+  // Dense: the waves of group A refill the ring. Sparse variants, whose
+  // scattered tiles have a longer fetch latency, spread it over all waves
+  // so that half of it is issued at the start of the period.
+  constexpr bool kFillB = SPARSE;
+  constexpr int NLOADER = kFillB ? NW : NW / 2;
   constexpr int STAGE_LOADS = STAGE / (NLOADER * 1024);  // 1 KB loads per loader wave per stage
   static_assert(STAGE % (NLOADER * 1024) == 0, "stage must split into whole 1 KB wave loads");
   static_assert(NS >= 2 && STAGE_LOADS * (NS - 2) < 64, "vmcnt range");
@@ -135,9 +140,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   }
 
   // Fill the stage of loop tile j: K of tile j and V of tile j-1 (blocks
-  // 0 .. STAGE/1024-1 of the stage; K first). Load r of loader wave w (the
-  // waves of group A) moves block r*NLOADER + w. At the ends (no V_{-1}, no
-  // K_nt) a neighbouring tile is copied
+  // 0 .. STAGE/1024-1 of the stage; K first). Load r of loader wave w moves
+  // block r*NLOADER + w. At the ends (no V_{-1}, no K_nt) a neighbouring
+  // tile is copied
   // into the unused half so that every stage costs each loader wave exactly
   // STAGE_LOADS loads (the vmcnt arithmetic below relies on it). tk and tv
   // are the workspace tiles of loop tiles j and j-1.
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       const int t = qidx[pos];
       pos = t < 0 ? 0 : (t < N ? t : N - 1);
     }
-    if (group == 0)
+    if (kFillB || group == 0)
       for (int j = 0; j < NS - 1; ++j)
         if (j <= nt) issue(j, tile_at(j), tile_at(j - 1));
     // grid coordinates of the row, once
@@ -509,7 +514,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // "refill" loops below; the "drain" loops follow). The waves of group A
   // issue it at the start of their softmax phase: group B's softmax runs
   // beside group A's GEMM phase, gets few vector issue slots there and is
-  // the longer path through the period, so it carries none of the refill.
+  // the longer path through the period, so in the dense kernel it carries
+  // none of the refill (sparse variants: its share, at the period start).
   // Softmax phase of workspace tile t in period i: the refill of tile
   // fill_tile (FILL), the list read for period i + 1, then the softmax
   // itself, during which the read lands. The scheduling barrier keeps the
@@ -557,10 +563,26 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     tile_barrier(nt);
     gemm(T{}, F{}, nt);
   } else {  // period i: SOFTMAX_{i-1} then GEMM_i (period 0: GEMM_0 only)
+    if constexpr (kFillB) {
+      if (NS - 1 <= nt) issue(NS - 1, tile_k(NS, 0), tile_k(NS - 1, 0));
+      __builtin_amdgcn_sched_barrier(0);
+    }
     prefetch(0);
     lists_landed();
     gemm(F{}, T{}, 0);
-    for (int j = 1; j < nt; ++j) {
+    int j = 1;
+    if constexpr (kFillB) {
+      for (; j < nt && j + NS - 1 <= nt; ++j) {
+        advance();
+        tile_barrier(j);
+        issue(j + NS - 1, tile_k(NS, j), tile_k(NS - 1, j));
+        __builtin_amdgcn_sched_barrier(0);  // the refill share ahead of the softmax arithmetic
+        sm(F{}, tile_k(0, j), 0, j);
+        lists_landed();
+        gemm(T{}, T{}, j);
+      }
+    }
+    for (; j < nt; ++j) {
       advance();
       tile_barrier(j);
       sm(F{}, tile_k(0, j), 0, j);
