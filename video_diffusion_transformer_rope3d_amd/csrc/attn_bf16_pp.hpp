@@ -142,10 +142,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // Fill the stage of loop tile j: K of tile j and V of tile j-1 (blocks
   // 0 .. STAGE/1024-1 of the stage; K first). Load r of loader wave w moves
   // block r*NLOADER + w. At the ends (no V_{-1}, no K_nt) a neighbouring
-  // tile is copied
-  // into the unused half so that every stage costs each loader wave exactly
-  // STAGE_LOADS loads (the vmcnt arithmetic below relies on it). tk and tv
-  // are the workspace tiles of loop tiles j and j-1.
+  // tile is copied into the unused half so that every stage costs each
+  // loader wave exactly STAGE_LOADS loads (the vmcnt arithmetic below relies
+  // on it). tk and tv are the workspace tiles of loop tiles j and j-1.
   auto issue_one = [&](int j, int r, int tk, int tv) __attribute__((always_inline)) {
     constexpr int KBLK = TILE / 1024;
     const int blk = r * NLOADER + wave;

@@ -96,14 +96,6 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Workgroup barrier without a memory fence. __syncthreads() also drains
-// every outstanding global load (vmcnt(0)), which would wait for the
-// direct-to-LDS prefetches of later pipeline stages too; callers wait with
-// an explicit, counted vmcnt for exactly the loads that must have landed.
-// The memory clobber keeps the compiler from moving LDS accesses across it,
-// and lgkmcnt(0) retires this wave's LDS reads before others may refill.
-// (The wait is the builtin, not inline asm, so the compiler's wait-count
-// tracking knows every LDS/scalar load has retired here.)
 // Direct global -> LDS copy of 16 bytes per lane: lane i reads base + voff
 // (base uniform, in SGPRs; voff per lane) and the data lands at LDS byte
 // address lds + 16 i. Written as inline assembly so that the compiler does
@@ -117,6 +109,14 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
                : "memory", "m0");
 }
 
+// Workgroup barrier without a memory fence. __syncthreads() also drains
+// every outstanding global load (vmcnt(0)), which would wait for the
+// direct-to-LDS prefetches of later pipeline stages too; callers wait with
+// an explicit, counted vmcnt for exactly the loads that must have landed.
+// The memory clobber keeps the compiler from moving LDS accesses across it,
+// and lgkmcnt(0) retires this wave's LDS reads before others may refill.
+// (The wait is the builtin, not inline asm, so the compiler's wait-count
+// tracking knows every LDS/scalar load has retired here.)
 __device__ __forceinline__ void lds_barrier() {
   constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);  // lgkmcnt(0), vmcnt/expcnt untouched
   // The scheduling barriers keep arithmetic on its side of the workgroup

@@ -57,8 +57,8 @@ constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxBH = int64_t(1) << 20;
 
 // bf16 attention kernel: 8 waves of 32 queries per workgroup, a ring of
-// VIDATTN_BF16_NS LDS stages of 64 keys (compile-time tuning knobs, with
-// VIDATTN_BF16_FILL_IN_S in attn_bf16_pp.hpp).
+// VIDATTN_BF16_NS LDS stages of 64 keys (a compile-time tuning knob; the
+// library ships three stages).
 #ifndef VIDATTN_BF16_NS
 #define VIDATTN_BF16_NS 3
 #endif
