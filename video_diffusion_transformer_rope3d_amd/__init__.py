@@ -292,12 +292,11 @@ def attention(q, k, v, *, scale=None, grid=None, split=None, theta=10000.0, out=
     otherwise they are used as given."""
     B, H, N, d = q.shape
     _check_qkv(q, k, v)
-    if out is None:
-        out = _torch().empty_like(q)
+    out = _out(out, q)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
     if workspace is None:
         workspace = workspace_for(q, rope is not None)
-    ws_ptr, ws_bytes = _ws(workspace)
+    ws_ptr, ws_bytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(q), B, H, N, d, s, rope,
                        ws_ptr, ws_bytes, _stream(stream)))
@@ -311,11 +310,42 @@ def _check_qkv(q, k, v):
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous [B, heads, N, d]")
+    _on_gpu(q)
 
 
-def _ws(workspace):
+def _on_gpu(ref, **tensors):
+    """The library takes device pointers: ref and every tensor given (None
+    skipped) must be contiguous and on ref's GPU."""
+    if not ref.is_cuda:
+        raise ValueError(f"tensors must be on a GPU, got {ref.device}")
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _out(out, ref, dtype=None):
+    """The output tensor: a new one shaped like ref, or the caller's, checked
+    for ref's shape, the dtype and ref's device."""
+    torch = _torch()
+    dtype = ref.dtype if dtype is None else dtype
+    if out is None:
+        return torch.empty(ref.shape, dtype=dtype, device=ref.device)
+    if tuple(out.shape) != tuple(ref.shape) or out.dtype != dtype:
+        raise ValueError(f"out must be a {dtype} tensor of shape {tuple(ref.shape)}, got {out.dtype} "
+                         f"{tuple(out.shape)}")
+    _on_gpu(ref, out=out)
+    return out
+
+
+def _ws(workspace, ref=None):
     if workspace is None:
         return None, 0
+    if ref is not None:
+        _on_gpu(ref, workspace=workspace)
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
@@ -327,7 +357,7 @@ def prepare(k, v, *, grid=None, split=None, theta=10000.0, workspace=None, strea
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
     if workspace is None:
         workspace = workspace_for(k, rope is not None)
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, k)
     _raise(vidattn_fwd_prepare(k.data_ptr(), v.data_ptr(), _dt(k), B, H, N, d, rope, ptr, nbytes,
                                _stream(stream)))
     return workspace
@@ -338,10 +368,9 @@ def attend(q, k, v, workspace, *, scale=None, grid=None, split=None, theta=10000
     image ``prepare`` wrote for k, v with the same rotary arguments."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
-    if out is None:
-        out = _torch().empty_like(q)
+    out = _out(out, q)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s,
                               rope, nbytes, _stream(stream)))
@@ -355,12 +384,12 @@ def attend_subset(q, q_index, workspace, N, *, scale=None, grid=None, split=None
     key/value image ``prepare`` wrote (BF16)."""
     torch = _torch()
     B, H, Nq, d = q.shape
-    if q_index.dtype != torch.int32 or q_index.dim() != 1 or q_index.numel() != Nq or not q_index.is_contiguous():
+    _on_gpu(q, q=q, q_index=q_index)
+    if q_index.dtype != torch.int32 or q_index.dim() != 1 or q_index.numel() != Nq:
         raise ValueError("q_index must be a contiguous int32 vector with one entry per query row")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(out, q)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd_attend_subset(q.data_ptr(), q_index.data_ptr(), Nq, ptr, out.data_ptr(), _dt(q), B, H, N, d,
                                      s, rope, nbytes, _stream(stream)))
@@ -376,16 +405,16 @@ def attend_block_sparse(q, workspace, kv_blocks, kv_count, *, scale=None, grid=N
     torch = _torch()
     B, H, N, d = q.shape
     nqb = -(-N // SPARSE_Q_BLOCK)
+    _on_gpu(q, q=q, kv_blocks=kv_blocks, kv_count=kv_count)
     if kv_blocks.dtype != torch.int32 or kv_count.dtype != torch.int32:
         raise ValueError("kv_blocks and kv_count must be int32")
     if kv_blocks.dim() != 4 or tuple(kv_blocks.shape[:3]) != (B, H, nqb) or not kv_blocks.is_contiguous():
         raise ValueError(f"kv_blocks must be a contiguous [{B}, {H}, {nqb}, max_blocks] tensor")
     if tuple(kv_count.shape) != (B, H, nqb) or not kv_count.is_contiguous():
         raise ValueError(f"kv_count must be a contiguous [{B}, {H}, {nqb}] tensor")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(out, q)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd_attend_block_sparse(q.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s, rope,
                                            kv_blocks.data_ptr(), kv_count.data_ptr(), kv_blocks.shape[3], nbytes,
@@ -414,12 +443,12 @@ def attend_block_mask(q, workspace, mask, *, scale=None, grid=None, split=None, 
     torch = _torch()
     B, H, N, d = q.shape
     nqb, nkb = -(-N // SPARSE_Q_BLOCK), -(-N // SPARSE_K_BLOCK)
+    _on_gpu(q, q=q, mask=mask)
     if mask.dtype != torch.int32 or tuple(mask.shape) != (B, H, nqb, -(-nkb // 32)) or not mask.is_contiguous():
         raise ValueError(f"mask must be a contiguous int32 [{B}, {H}, {nqb}, {-(-nkb // 32)}] tensor")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(out, q)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd_attend_block_mask(q.data_ptr(), mask.data_ptr(), ptr, out.data_ptr(), _dt(q), B, H, N, d, s,
                                          rope, nbytes, _stream(stream)))
@@ -434,14 +463,13 @@ def window_attention(q, k, v, radius, *, grid, split=None, theta=10000.0, scale=
     torch = _torch()
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out(out, q)
     rd = Rope3dDesc.make(grid, split, theta) if rope else None
     wd = WindowDesc.make(grid, radius)
     if workspace is None:
         n = vidattn_fwd_window_workspace_size(_dt(q), B, H, N, d, rope)
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(q), B, H, N, d, s, rd, wd,
                               ptr, nbytes, _stream(stream)))
@@ -455,13 +483,11 @@ def rope3d(x, grid, split, theta=10000.0, *, token_offset=None, out=None, out_dt
     without it, x holds the whole grid."""
     torch = _torch()
     B, H, N, d = x.shape
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
+    _on_gpu(x, x=x)
     n_grid = int(grid[0]) * int(grid[1]) * int(grid[2])
     if token_offset is None and N != n_grid:
         raise ValueError(f"x has {N} tokens, grid {tuple(grid)} has {n_grid}")
-    if out is None:
-        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    out = _out(out, x, out_dtype or (out.dtype if out is not None else x.dtype))
     desc = Rope3dDesc.make(grid, split, theta)
     if token_offset is None:
         _raise(vidattn_rope3d(x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), B, H, d, desc, prescale,
