@@ -103,7 +103,9 @@ __device__ __forceinline__ float xor32_sum(float v) {
 // wait in the same loop becomes lgkmcnt(0), which drains the operand
 // double buffer at every other MFMA batch. The caller orders these copies
 // with explicit vmcnt waits and barriers. (m0 holds the LDS address; the
-// nop covers the m0 write before the LDS DMA.)
+// nop covers the m0 write before the LDS DMA. The compiler reserves m0 and
+// warns about the clobber; it is sound because the kernels use m0 nowhere
+// else, which tests/test_sources.py checks on the generated assembly.)
 __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
                : "memory", "m0");
