@@ -143,7 +143,8 @@ vidattn_status vidattn_rope3d_tokens(const void* in, vidattn_dtype in_dt, void* 
  *                 overwritten.
  * All N keys are attended by every query (no mask, no causal order).
  * Pointers must be 16-byte aligned; o must not overlap q, k, v or the
- * workspace. */
+ * workspace, and the workspace (which the pre-pass writes before q is read)
+ * must not overlap q, k or v; INVALID_ARG otherwise. */
 vidattn_status vidattn_fwd(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt,
                            int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
                            const vidattn_rope3d_desc* rope, void* workspace, size_t workspace_bytes,
@@ -209,9 +210,9 @@ vidattn_status vidattn_fwd_attend_subset(const void* q, const int32_t* q_index, 
 /* Block-sparse attention against a prepared key/value set: each query block
  * attends only to the key blocks listed for it: the block-sparse video-DiT
  * attention of ScalingAttention (a bit-wise block-sparse kernel driven by a
- * per-head block mask) and of Sparse Forcing's Persistent Block-Sparse
- * Attention (their abstracts on the paper listing
- * thelatestinai.com/papers/2606.17566). Logits of unlisted key blocks are
+ * per-head block mask; its abstract on thelatestinai.com/papers/2606.17566)
+ * and of Sparse Forcing's Persistent Block-Sparse Attention (its abstract on
+ * thelatestinai.com/papers/2609.18077). Logits of unlisted key blocks are
  * -inf before the softmax; a query block with no listed key block gets O = 0
  * (a reading: the pages do not define that case).
  *   q, o        [B][heads][N][d] BF16.
@@ -261,7 +262,9 @@ typedef struct {
  *              first vidattn_fwd_workspace_size bytes, and room after it for
  *              the lists built from the mask: at least
  *              vidattn_fwd_block_mask_workspace_size(...) bytes in all.
- *   q, o       [B][heads][N][d] BF16; o must not overlap q or the workspace.
+ *   q, o       [B][heads][N][d] BF16; o must not overlap q or the workspace,
+ *              and q must not overlap the list part of the workspace (it is
+ *              written before q is read).
  * A query block with no bit set gets O = 0. Only BF16 is implemented (F32:
  * UNSUPPORTED). Other arguments as for vidattn_fwd_attend. */
 vidattn_status vidattn_fwd_attend_block_mask(const void* q, const uint32_t* mask, void* workspace, void* o,
@@ -279,14 +282,15 @@ size_t vidattn_fwd_block_mask_workspace_size(vidattn_dtype dt, int64_t B, int64_
  * window, the windowed-attention primitive of the vidax summary
  * (paperlayer.ai/abs/2609.18077v1, "2 System Architecture & Design", heading
  * "3D RoPE, 3D VAEs, and flash attention") and the sliding local windows of
- * Sparse Forcing (its abstract on thelatestinai.com/papers/2606.17566); the
+ * Sparse Forcing (its abstract on thelatestinai.com/papers/2609.18077); the
  * pages fix no window shape, the centred box above is the plainest reading.
  * One call runs the key/value pre-pass, a planning kernel that lists per
  * 256-query block the 64-key tiles of the grid rows its queries' windows
  * reach (in the workspace), and the attention over those tiles with the keys
  * outside each query's box masked. Arguments as for vidattn_fwd, plus:
  *   window     non-null; its grid must equal rope's when rope is given.
- *   workspace  at least vidattn_fwd_window_workspace_size(...) bytes.
+ *   workspace  at least vidattn_fwd_window_workspace_size(...) bytes; as
+ *              for vidattn_fwd it must not overlap q, k, v or o.
  * An unbounded window gives the vidattn_fwd result bit for bit. Only BF16 is
  * implemented (F32: UNSUPPORTED). */
 vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,

@@ -170,8 +170,9 @@ def block_sparse_mask(N: int, kv_blocks, kv_count, q_block: int, k_block: int) -
 def block_sparse_attention(q, k, v, grid, split, theta, scale, kv_blocks, kv_count, q_block=256, k_block=64,
                            rows=None) -> np.ndarray:
     """Block-sparse attention of one (batch, head) slice, the block-sparse
-    video-DiT attention of ScalingAttention and of Persistent Block-Sparse
-    Attention (their abstracts on thelatestinai.com/papers/2606.17566): the
+    video-DiT attention of ScalingAttention (its abstract on
+    thelatestinai.com/papers/2606.17566) and of Sparse Forcing's Persistent
+    Block-Sparse Attention (its abstract on thelatestinai.com/papers/2609.18077): the
     logits of keys outside the listed blocks are -inf before the softmax. A
     query whose block lists no key block has no attended key; its output is
     defined as 0 (a reading: the pages leave that case open). q, k, v are
@@ -252,7 +253,7 @@ def window_attention(q, k, v, grid, split, theta, scale, radius, rows=None, rope
     only to the keys inside a box of radii (r_f, r_h, r_w) around its own
     grid position (the windowed-attention primitive of the vidax summary,
     "3D RoPE, 3D VAEs, and flash attention", and the sliding local windows of
-    Sparse Forcing's abstract on thelatestinai.com/papers/2606.17566; the
+    Sparse Forcing's abstract on thelatestinai.com/papers/2609.18077; the
     pages give no window shape, a centred box clipped at the border is the
     plainest reading). Every query sees at least itself."""
     N = np.asarray(q).shape[0]

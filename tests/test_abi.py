@@ -293,3 +293,24 @@ def test_build_entry_checks_the_binding_abi():
     import inspect
     src = inspect.getsource(entry.build)
     assert "va.ABI_VERSION" in src and "== 3" not in src
+
+
+def test_workspace_writers_reject_q_in_the_workspace():
+    """The calls that write the workspace before the attention kernel reads q
+    (the fused call, the window call, the block-mask list building) reject a
+    q that overlaps what they write; the attend phase, which only reads the
+    workspace, accepts it up to the launch (not made here)."""
+    wsb = va.vidattn_fwd_workspace_size(va.BF16, 2, 40, N5, 128, 1)
+    KF, VF = QF + T // 4, QF + T // 2
+    s = va.vidattn_fwd(WSF + 4096, KF, VF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD, WSF, wsb)
+    assert s == 1 and "q overlaps the workspace" in va.vidattn_last_error()
+    s = va.vidattn_fwd(WSF - 4096, KF, VF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD, WSF, wsb)
+    assert s == 1 and "q overlaps the workspace" in va.vidattn_last_error()
+    wwsb = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1)
+    W = va.WindowDesc.make((21, 45, 80), (1, 4, 4))
+    s = va.vidattn_fwd_window(WSF + wwsb - 4096, KF, VF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD, W, WSF, wwsb)
+    assert s == 1 and "q overlaps the workspace" in va.vidattn_last_error()
+    need = va.vidattn_fwd_block_mask_workspace_size(va.BF16, 2, 40, N5, 128, True)
+    MK = 6 << 40
+    s = va.vidattn_fwd_attend_block_mask(WSF + wsb, MK, WSF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD, need, None)
+    assert s == 1 and "q overlaps the list part" in va.vidattn_last_error()

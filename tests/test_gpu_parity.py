@@ -332,3 +332,127 @@ def test_two_phase_equals_fused_bitwise(va, dt, rope):
     torch.cuda.synchronize()
     iv = torch.int16 if dt == "bf16" else torch.int32
     assert torch.equal(fused.view(iv), a1.view(iv)) and torch.equal(a1.view(iv), a2.view(iv))
+
+
+# ------------------------------------------------------------------ softmax edge cases
+# The kernel keeps the running maximum lazily: it redoes a tile against the
+# exact maximum only when some probability exp2(s - m - 20) reaches 2. These
+# cases drive each branch of that rule, dense, block-sparse and windowed,
+# against the oracle on every row. Flash attention must reproduce the plain
+# softmax exactly (vidax summary, "2 System Architecture & Design", heading
+# "3D RoPE, 3D VAEs, and flash attention"), so the bound is the usual bf16 one.
+
+EDGE_N, EDGE_D = 1000, 128
+EDGE_CASES = {
+    # a late key 25-34 log2 units above the running maximum (finite exact step),
+    # then a later one 111-167 above it (exp2 overflows to +inf for most rows)
+    "late_dominant": [[(330, 2.0), (600, 10.5)], [(700, 2.0), (980, 10.5)]],
+    # the first tile holds the maximum of every row: by ~48 and by ~7 log2 units
+    "first_tile_dominant": [[(5, 3.75)], [(40, 0.5)]],
+    # identical key rows in several tiles (and twice in one tile): exact ties
+    "ties": [[(100, 4.0), (101, 4.0), (500, 4.0), (900, 4.0)], [(63, 4.0), (64, 4.0), (999, 4.0)]],
+}
+
+
+def _edge_inputs(case):
+    q, k, v = wlmod.planted_keys(EDGE_N, EDGE_D, 2, EDGE_CASES[case])
+    return q, k, v
+
+
+def _edge_compare(got_t, ref_fn, heads=2):
+    got = parity.from_torch(got_t)
+    err = ref = 0.0
+    worst = 0.0
+    for h in range(heads):
+        r = ref_fn(h)
+        e = np.abs(got[0, h] - r)
+        worst = max(worst, float(e.max()))
+        err += float(e.sum())
+        ref += float(np.abs(r).sum())
+    assert np.isfinite(got).all()
+    assert worst <= 2e-2 and err / ref <= 5e-3, (worst, err / ref)
+    return worst, err / ref
+
+
+@pytest.mark.parametrize("case", sorted(EDGE_CASES))
+def test_softmax_edge_dense(va, case):
+    _log(f"softmax edge dense {case}")
+    qh, kh, vh = _edge_inputs(case)
+    q, k, v = (parity.to_torch(x) for x in (qh, kh, vh))
+    scale = 1.0 / math.sqrt(EDGE_D)
+    o = va.attention(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    dec = oracle.decode_bf16
+    stats = _edge_compare(o, lambda h: oracle.attention(dec(qh[0, h]), dec(kh[0, h]), dec(vh[0, h]), scale))
+    _log(f"  max-abs {stats[0]:.3e} mean-rel {stats[1]:.3e}")
+
+
+@pytest.mark.parametrize("case", sorted(EDGE_CASES))
+def test_softmax_edge_block_sparse(va, case):
+    _log(f"softmax edge block-sparse {case}")
+    qh, kh, vh = _edge_inputs(case)
+    q, k, v = (parity.to_torch(x) for x in (qh, kh, vh))
+    scale = 1.0 / math.sqrt(EDGE_D)
+    nqb = -(-EDGE_N // va.SPARSE_Q_BLOCK)
+    # query block 0: the early and the planted tiles; 1: everything but tiles
+    # 9 and 15; 2: tile 9 alone; 3: the ragged last tile alone
+    lists = [[0, 1, 5, 7, 9, 10, 14, 15], [t for t in range(16) if t not in (9, 15)], [9], [15]]
+    width = max(len(x) for x in lists)
+    blocks = np.full((1, 2, nqb, width), -1, dtype=np.int32)
+    count = np.zeros((1, 2, nqb), dtype=np.int32)
+    for h in range(2):
+        for i, x in enumerate(lists):
+            blocks[0, h, i, :len(x)] = x
+            count[0, h, i] = len(x)
+    ws = va.prepare(k, v)
+    o = va.attend_block_sparse(q, ws, torch.from_numpy(blocks).cuda(), torch.from_numpy(count).cuda(), scale=scale)
+    torch.cuda.synchronize()
+    dec = oracle.decode_bf16
+    stats = _edge_compare(o, lambda h: oracle.block_sparse_attention(
+        dec(qh[0, h]), dec(kh[0, h]), dec(vh[0, h]), None, None, None, scale, blocks[0, h], count[0, h],
+        va.SPARSE_Q_BLOCK, va.SPARSE_K_BLOCK))
+    _log(f"  max-abs {stats[0]:.3e} mean-rel {stats[1]:.3e}")
+
+
+@pytest.mark.parametrize("case", sorted(EDGE_CASES))
+@pytest.mark.parametrize("grid,radius", [((4, 10, 25), (1, 3, 6)), ((2, 4, 125), (1, 1, 20))])
+def test_softmax_edge_window(va, case, grid, radius):
+    _log(f"softmax edge window {case} grid={grid} radius={radius}")
+    qh, kh, vh = _edge_inputs(case)
+    q, k, v = (parity.to_torch(x) for x in (qh, kh, vh))
+    scale = 1.0 / math.sqrt(EDGE_D)
+    o = va.window_attention(q, k, v, radius, grid=grid, rope=False, scale=scale)
+    torch.cuda.synchronize()
+    dec = oracle.decode_bf16
+    stats = _edge_compare(o, lambda h: oracle.window_attention(
+        dec(qh[0, h]), dec(kh[0, h]), dec(vh[0, h]), grid, None, None, scale, radius, rope=False))
+    _log(f"  max-abs {stats[0]:.3e} mean-rel {stats[1]:.3e}")
+
+
+def test_side_stream_buffers_follow_the_stream(va):
+    """attention() on a side stream, workspace and output left to the
+    binding: both are allocated on that stream, so the caching allocator
+    cannot hand the dropped workspace to work queued on the current stream
+    while the side stream's kernels still use it. Allocations filled with
+    junk on the current stream right after each call must not disturb the
+    result (bit for bit against the same call on the current stream)."""
+    wl = wlmod.custom(1, 4, (6, 20, 64), 128, (44, 42, 42), seed_id=911)
+    _log(f"side stream {wl.name}")
+    host = parity.host_inputs(wl)
+    q, k, v = (parity.to_torch(host[n]) for n in ("q", "k", "v"))
+    kw = dict(scale=wl.scale, grid=wl.grid, split=wl.split, theta=wl.theta)
+    ref = va.attention(q, k, v, **kw)
+    torch.cuda.synchronize()
+    nbytes = va.vidattn_fwd_workspace_size(va.BF16, wl.B, wl.heads, wl.N, wl.d, True)
+    side = torch.cuda.Stream()
+    for _ in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        o = va.attention(q, k, v, stream=side, **kw)
+        junk = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        junk.fill_(0xFF)
+        junk_o = torch.empty_like(q)
+        junk_o.fill_(float("nan"))
+        torch.cuda.current_stream().wait_stream(side)
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+        del junk, junk_o
+    torch.cuda.synchronize()

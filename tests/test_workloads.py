@@ -61,3 +61,30 @@ def test_sample_rows():
     assert r[0] == 0 and r[-1] == w.N - 1
     assert np.array_equal(r, wl.sample_rows(w, 1, 7))
     assert np.array_equal(wl.sample_rows(wl.WORKLOADS[1], 0, 0), np.arange(256))
+
+
+def test_planted_keys_drive_the_intended_softmax_course():
+    """The planted-key inputs of the GPU softmax edge cases do what the
+    cases claim, checked on the decoded values: the late keys lift the
+    running maximum by more than the exact-step threshold (21 log2 units),
+    the largest by enough to overflow exp2(s - m - 20) in fp32 for some rows;
+    a first-tile key dominates every later key; tied keys are identical."""
+    import oracle
+    from tests.test_gpu_parity import EDGE_CASES, EDGE_D, EDGE_N
+    q, k, v = wl.planted_keys(EDGE_N, EDGE_D, 2, EDGE_CASES["late_dominant"])
+    for h, ((j1, _), (j2, _)) in enumerate(EDGE_CASES["late_dominant"]):
+        qd, kd = oracle.decode_bf16(q[0, h]), oracle.decode_bf16(k[0, h])
+        s = qd @ kd.T / np.sqrt(EDGE_D) * np.log2(np.e)
+        before1 = s[:, :j1 // 64 * 64].max(axis=1)
+        assert (s[:, j1] - before1).min() > 21
+        assert (s[:, j2] - s[:, j1] - 20).max() > 128  # exp2 overflows for these rows
+    q, k, v = wl.planted_keys(EDGE_N, EDGE_D, 2, EDGE_CASES["first_tile_dominant"])
+    for h, ((j, _),) in enumerate(EDGE_CASES["first_tile_dominant"]):
+        assert j < 64
+        qd, kd = oracle.decode_bf16(q[0, h]), oracle.decode_bf16(k[0, h])
+        s = qd @ kd.T
+        assert (s[:, j] > np.delete(s, j, axis=1).max(axis=1)).all()
+    q, k, v = wl.planted_keys(EDGE_N, EDGE_D, 2, EDGE_CASES["ties"])
+    for h, plants in enumerate(EDGE_CASES["ties"]):
+        rows = [k[0, h, j] for j, _ in plants]
+        assert all(np.array_equal(rows[0], r) for r in rows[1:])

@@ -275,14 +275,35 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
-def workspace_for(q, use_rope: bool):
-    """A torch byte buffer of the size vidattn_fwd needs for q's shape (None if 0)."""
+def _torch_stream(stream, device):
+    """The stream the kernels will run on, as a torch stream object."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)), device=device)
+
+
+def _empty(shape, dtype, device, stream):
+    """A new device tensor owned by the stream the kernels run on: the caching
+    allocator then reuses its memory only in that stream's order, so a buffer
+    the binding drops on return cannot be handed to work on another stream
+    while the kernels still read or write it."""
+    torch = _torch()
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def workspace_for(q, use_rope: bool, stream=None):
+    """A torch byte buffer of the size vidattn_fwd needs for q's shape (None if
+    0), allocated on ``stream`` (default: the current stream)."""
     torch = _torch()
     B, H, N, d = q.shape
     n = vidattn_fwd_workspace_size(_dt(q), B, H, N, d, use_rope)
     if n == 0:
         return None
-    return torch.empty(n, dtype=torch.uint8, device=q.device)
+    return _empty(n, torch.uint8, q.device, stream)
 
 
 def attention(q, k, v, *, scale=None, grid=None, split=None, theta=10000.0, out=None, workspace=None,
@@ -292,10 +313,10 @@ def attention(q, k, v, *, scale=None, grid=None, split=None, theta=10000.0, out=
     otherwise they are used as given."""
     B, H, N, d = q.shape
     _check_qkv(q, k, v)
-    out = _out(out, q)
+    out = _out(out, q, stream=stream)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
     if workspace is None:
-        workspace = workspace_for(q, rope is not None)
+        workspace = workspace_for(q, rope is not None, stream)
     ws_ptr, ws_bytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(q), B, H, N, d, s, rope,
@@ -327,13 +348,13 @@ def _on_gpu(ref, **tensors):
             raise ValueError(f"{name} must be contiguous")
 
 
-def _out(out, ref, dtype=None):
-    """The output tensor: a new one shaped like ref, or the caller's, checked
-    for ref's shape, the dtype and ref's device."""
-    torch = _torch()
+def _out(out, ref, dtype=None, stream=None):
+    """The output tensor: a new one shaped like ref (allocated on the stream
+    the kernels run on), or the caller's, checked for ref's shape, the dtype
+    and ref's device."""
     dtype = ref.dtype if dtype is None else dtype
     if out is None:
-        return torch.empty(ref.shape, dtype=dtype, device=ref.device)
+        return _empty(ref.shape, dtype, ref.device, stream)
     if tuple(out.shape) != tuple(ref.shape) or out.dtype != dtype:
         raise ValueError(f"out must be a {dtype} tensor of shape {tuple(ref.shape)}, got {out.dtype} "
                          f"{tuple(out.shape)}")
@@ -356,7 +377,7 @@ def prepare(k, v, *, grid=None, split=None, theta=10000.0, workspace=None, strea
     B, H, N, d = k.shape
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
     if workspace is None:
-        workspace = workspace_for(k, rope is not None)
+        workspace = workspace_for(k, rope is not None, stream)
     ptr, nbytes = _ws(workspace, k)
     _raise(vidattn_fwd_prepare(k.data_ptr(), v.data_ptr(), _dt(k), B, H, N, d, rope, ptr, nbytes,
                                _stream(stream)))
@@ -368,7 +389,7 @@ def attend(q, k, v, workspace, *, scale=None, grid=None, split=None, theta=10000
     image ``prepare`` wrote for k, v with the same rotary arguments."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
-    out = _out(out, q)
+    out = _out(out, q, stream=stream)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
     ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -387,7 +408,7 @@ def attend_subset(q, q_index, workspace, N, *, scale=None, grid=None, split=None
     _on_gpu(q, q=q, q_index=q_index)
     if q_index.dtype != torch.int32 or q_index.dim() != 1 or q_index.numel() != Nq:
         raise ValueError("q_index must be a contiguous int32 vector with one entry per query row")
-    out = _out(out, q)
+    out = _out(out, q, stream=stream)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
     ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -412,7 +433,7 @@ def attend_block_sparse(q, workspace, kv_blocks, kv_count, *, scale=None, grid=N
         raise ValueError(f"kv_blocks must be a contiguous [{B}, {H}, {nqb}, max_blocks] tensor")
     if tuple(kv_count.shape) != (B, H, nqb) or not kv_count.is_contiguous():
         raise ValueError(f"kv_count must be a contiguous [{B}, {H}, {nqb}] tensor")
-    out = _out(out, q)
+    out = _out(out, q, stream=stream)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
     ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -446,7 +467,7 @@ def attend_block_mask(q, workspace, mask, *, scale=None, grid=None, split=None, 
     _on_gpu(q, q=q, mask=mask)
     if mask.dtype != torch.int32 or tuple(mask.shape) != (B, H, nqb, -(-nkb // 32)) or not mask.is_contiguous():
         raise ValueError(f"mask must be a contiguous int32 [{B}, {H}, {nqb}, {-(-nkb // 32)}] tensor")
-    out = _out(out, q)
+    out = _out(out, q, stream=stream)
     rope = Rope3dDesc.make(grid, split, theta) if grid is not None else None
     ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -463,12 +484,12 @@ def window_attention(q, k, v, radius, *, grid, split=None, theta=10000.0, scale=
     torch = _torch()
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
-    out = _out(out, q)
+    out = _out(out, q, stream=stream)
     rd = Rope3dDesc.make(grid, split, theta) if rope else None
     wd = WindowDesc.make(grid, radius)
     if workspace is None:
         n = vidattn_fwd_window_workspace_size(_dt(q), B, H, N, d, rope)
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+        workspace = _empty(n, torch.uint8, q.device, stream) if n else None
     ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _raise(vidattn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(q), B, H, N, d, s, rd, wd,
@@ -487,7 +508,7 @@ def rope3d(x, grid, split, theta=10000.0, *, token_offset=None, out=None, out_dt
     n_grid = int(grid[0]) * int(grid[1]) * int(grid[2])
     if token_offset is None and N != n_grid:
         raise ValueError(f"x has {N} tokens, grid {tuple(grid)} has {n_grid}")
-    out = _out(out, x, out_dtype or (out.dtype if out is not None else x.dtype))
+    out = _out(out, x, out_dtype or (out.dtype if out is not None else x.dtype), stream=stream)
     desc = Rope3dDesc.make(grid, split, theta)
     if token_offset is None:
         _raise(vidattn_rope3d(x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), B, H, d, desc, prescale,

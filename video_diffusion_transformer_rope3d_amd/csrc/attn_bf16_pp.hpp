@@ -10,7 +10,8 @@
 // Per wave and tile j there are two phases:
 //   GEMM_j     O^T += V_{j-1}^T P_{j-1}^T   (16 x v_mfma_f32_32x32x16_bf16)
 //              S'^T = K_j Q'^T - m          (16 x v_mfma_f32_32x32x16_f16)
-//   SOFTMAX_j  P_j = exp2(S'_j) -> bf16, row sums, rare exact rescale
+//   SOFTMAX_j  P_j = exp2(S'_j) -> bf16, rare exact rescale, row sums
+//              (group B adds its row sums in its next GEMM phase)
 // Waves 0-3 (group A) and 4-7 (group B) sit one per SIMD each (the hardware
 // places wave w and w+4 of a workgroup on the same SIMD). One barrier opens
 // each tile period; in it group A runs GEMM then SOFTMAX and group B runs
@@ -26,10 +27,13 @@
 // split them with group B, which issues its share at the period start).
 //
 // Numerics: the transposed products put all
-// scores and outputs of query q in lanes q and q+32, the running maximum m
-// enters as the accumulator input of the first score MFMA, and m moves only
-// when a tile's probability sum exceeds 2^20 (then the tile is redone against
-// the exact maximum and O, l are scaled).
+// scores and outputs of query q in lanes q and q+32, and m + 20 (m the
+// running maximum, in log2 units) enters as the accumulator input of the
+// first score MFMA, so P = exp2(s - m - 20) is at most 2^-20 at the maximum.
+// m moves only when some probability of a tile reaches 2 (a score more than
+// 21 above m, or a non-finite one), which one bit of the OR of the bf16
+// probabilities shows; then the tile is redone against the exact maximum and
+// O, l are scaled. The common factor 2^-20 cancels in O / l.
 //
 // Three variants share the loop. Query subset: Nq query rows (Nq may differ
 // from the Nk keys) whose rotary positions are the token indices qidx[row]
@@ -91,7 +95,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   constexpr int STAGE_LOADS = STAGE / (NLOADER * 1024);  // 1 KB loads per loader wave per stage
   static_assert(STAGE % (NLOADER * 1024) == 0, "stage must split into whole 1 KB wave loads");
   static_assert(NS >= 2 && STAGE_LOADS * (NS - 2) < 64, "vmcnt range");
-  constexpr float kRescaleSum = 1048576.0f;  // 2^20
+  // The probabilities are exp2(s - m - kBias): at most 2^-20 for a score at
+  // the running maximum m, so a tile needs the exact step only when some
+  // probability reaches 2 (a score more than kBias + 1 above m, or a
+  // non-finite one): one bit of its bf16 exponent.
+  constexpr float kBias = 20.f;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
 
   const int lane = threadIdx.x & 63;
@@ -158,7 +166,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
 #pragma unroll
     for (int r = 0; r < STAGE_LOADS; ++r) issue_one(j, r, tk, tv);
   };
-
   // ---- queries: rotate, pre-scale by scale*log2(e), round to fp16 (B operand).
   // Their loads are issued before any tile load, so waiting for tile 0 covers them.
   half8 qreg[KSTEPS];
@@ -233,19 +240,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     wend = wp.W + chi + 1;
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) negm[i] = 0.f;
+  for (int i = 0; i < 16; ++i) negm[i] = -kBias;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-  // P = exp2(S') as bf16 B operands; returns the lane's partial sum of the
-  // rounded probabilities. Score register i of key block kb is key
-  // 32kb + 16(i/8) + 8g + i%8, so pk[ms] holds keys 16ms + 8g .. +7.
+  // P = exp2(S') as bf16 B operands. Score register i of key block kb is key
+  // 32kb + 16(i/8) + 8g + i%8, so pk[ms] holds keys 16ms + 8g .. +7. Returns
+  // the OR of the probabilities' bits (a balanced tree: it is on the path to
+  // the exact-step test).
   auto probs = [&]() __attribute__((always_inline)) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    float part[MS];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -253,15 +258,40 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         bf16x8 p;
 #pragma unroll
         for (int j = 0; j < 8; ++j) p[j] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * h + j]);
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x2 pp = {p[2 * j], p[2 * j + 1]};
-          acc = __builtin_amdgcn_fdot2_f32_bf16(pp, one, acc, false);
-        }
-        part[2 * kb + h] = acc;
         pk[2 * kb + h] = p;
       }
+    uint32_t w[4 * MS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const bf16x8 pv = pk[ms];
+      const u32x4 x = __builtin_bit_cast(u32x4, pv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[4 * ms + e] = x[e];
+    }
+    // (the empty asm statements keep the compiler from re-associating the
+    // tree into one serial chain)
+    uint32_t a = w[0] | w[1] | w[2], b = w[3] | w[4] | w[5], c = w[6] | w[7] | w[8];
+    uint32_t d = w[9] | w[10] | w[11], e = w[12] | w[13] | w[14];
+    asm("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e));
+    uint32_t f = a | b | c, h = d | e | w[15];
+    asm("" : "+v"(f), "+v"(h));
+    return f | h;
+  };
+  // The lane's partial row sum of the rounded probabilities.
+  auto rowsum = [&]() __attribute__((always_inline)) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float part[MS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 pp = {pk[ms][2 * j], pk[ms][2 * j + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pp, one, acc, false);
+      }
+      part[ms] = acc;
+    }
     return (part[0] + part[1]) + (part[2] + part[3]);
   };
 
@@ -393,12 +423,34 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // double-buffered in registers: batch b+1 is read while the MFMAs of
   // batch b run, so each MFMA finds its operand already loaded.
   constexpr int RB = 4;
-  auto gemm = [&](auto PV, auto SC, int jj) __attribute__((always_inline)) {
-    // one register holds this lane's address in the stage; the operand
-    // offsets (< 32 KB) then fit the ds_read immediate field
+  struct Batch {
+    u32x4 v[RB];
+    const uint8_t* st;  // the stage the batch was read from
+  };
+  // one register holds this lane's address in the stage; the operand
+  // offsets (< 32 KB) then fit the ds_read immediate field
+  auto stage_ptr = [&](int jj) __attribute__((always_inline)) {
     uint32_t sb = (uint32_t)(uintptr_t)(lds + (jj % NS) * STAGE + lane * 16);
     asm volatile("" : "+v"(sb));
-    const uint8_t* st = (const uint8_t*)(__attribute__((address_space(3))) const uint8_t*)(uintptr_t)sb;
+    return (const uint8_t*)(__attribute__((address_space(3))) const uint8_t*)(uintptr_t)sb;
+  };
+  // The first operand batch of a GEMM phase with the P.V product (V blocks
+  // 0 .. RB-1). Group B reads it right after the barrier, ahead of its
+  // softmax, so that its GEMM phase starts without an LDS wait.
+  auto first_batch = [&](int jj) __attribute__((always_inline)) {
+    const uint8_t* st = stage_ptr(jj);
+    Batch b;
+    b.st = st;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) b.v[r] = *reinterpret_cast<const u32x4*>(st + TILE + r * 1024);
+    __builtin_amdgcn_sched_barrier(0);  // issue the reads before what follows
+    return b;
+  };
+  // GEMM phase of tile jj: O^T += V_{jj-1}^T P^T (PV), S'^T = K_jj Q'^T - m
+  // (SC). SUM: add the row sums of the P being multiplied to l (in the shadow
+  // of the MFMAs). PRE: the first operand batch was read ahead (pre).
+  auto gemm = [&](auto PV, auto SC, int jj, auto SUM, auto PRE, const Batch& pre) __attribute__((always_inline)) {
+    const uint8_t* st = decltype(PRE)::value ? pre.st : stage_ptr(jj);
     constexpr int NV = decltype(PV)::value ? DB * MS : 0;  // V^T operand blocks
     constexpr int NK = decltype(SC)::value ? 2 * KSTEPS : 0;  // K operand blocks
     constexpr int NOP = NV + NK;
@@ -423,7 +475,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     }
     u32x4 buf[2][RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) buf[0][r] = *reinterpret_cast<const u32x4*>(addr(r));
+    for (int r = 0; r < RB; ++r) buf[0][r] = decltype(PRE)::value ? pre.v[r] : *reinterpret_cast<const u32x4*>(addr(r));
 #pragma unroll
     for (int b = 0; b < NOP / RB; ++b) {
       if (b + 1 < NOP / RB) {
@@ -444,10 +496,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         }
       }
     }
+    if constexpr (decltype(SUM)::value) l += rowsum();
     // keep the batch structure: RB reads up front, then (RB reads, RB MFMAs) per batch
 #pragma unroll
     for (int b = 0; b < NOP / RB; ++b) {
-      __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
+      if (b > 0 || !decltype(PRE)::value) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
       if (b > 0) __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);  // MFMA
     }
     __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
@@ -455,7 +508,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
 
   // SOFTMAX phase of the scores of workspace tile t (in the last tile, keys
   // past N get -inf).
-  auto softmax = [&](int t) __attribute__((always_inline)) {
+  // SUM: add the row sums to l here (else the next GEMM phase does).
+  auto softmax = [&](int t, auto SUM) __attribute__((always_inline)) {
     {
       if (tail < KT && t == nkt - 1) {
 #pragma unroll
@@ -467,11 +521,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           }
       }
     }
-    float ls = probs();
+    const bool big = (probs() & 0x40004000u) != 0u;  // some p >= 2 (or not finite)
     // the exact step: for a row's first tile with a visible key (a row with
-    // no visible key in this tile keeps m unset), and when the sum shows a
-    // score far above m
-    if (__builtin_amdgcn_ballot_w64((!m_valid && wvis != 0u) || !(ls <= kRescaleSum)) != 0) {
+    // no visible key in this tile keeps m unset), and when a score lies more
+    // than kBias + 1 above m
+    if (__builtin_amdgcn_ballot_w64((!m_valid && wvis != 0u) || big) != 0) {
       // exact maximum of the tile (relative to the current m); a row that
       // has seen no visible key yet takes the tile's maximum as its m (and
       // keeps m = 0 if the tile shows it none)
@@ -480,7 +534,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = xor32_max(mx);
+      mx = xor32_max(mx) + kBias;
       const bool seen = mx > -INFINITY;
       const float delta = !m_valid ? (seen ? mx : 0.f) : fmaxf(mx, 0.f);
       const float alpha = !m_valid ? 1.f : __builtin_amdgcn_exp2f(-delta);
@@ -492,14 +546,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       m += delta;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) negm[i] = -m;
+      for (int i = 0; i < 16; ++i) negm[i] = -(m + kBias);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] -= delta;
-      ls = probs();
+      probs();
     }
-    l += ls;
+    if constexpr (decltype(SUM)::value) l += rowsum();
   };
 
   using T = std::true_type;
@@ -522,11 +576,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   auto prefetch = [&](int i) __attribute__((always_inline)) {
     if constexpr (SPARSE) tnext = tile_at(i + NS);
   };
-  auto sm = [&](auto FILL, int t, int fill_tile, int i) __attribute__((always_inline)) {
+  auto sm = [&](auto FILL, int t, int fill_tile, int i, auto SUM) __attribute__((always_inline)) {
     if constexpr (SPARSE) __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(FILL)::value) issue(fill_tile, tile_k(NS, i), tile_k(NS - 1, i));
     prefetch(i);
-    softmax(t);
+    softmax(t, SUM);
   };
   // before a GEMM phase that no barrier precedes: no list read in flight
   auto lists_landed = [&]() __attribute__((always_inline)) {
@@ -537,38 +591,42 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  const Batch nob{};
   tile_barrier(0);
-  if (group == 0) {  // period i: GEMM_i then SOFTMAX_i
+  if (group == 0) {  // period i: GEMM_i then SOFTMAX_i (with the row sums)
     if (NS - 1 <= nt) {
-      gemm(F{}, T{}, 0);
-      sm(T{}, tile_k(1, 0), NS - 1, 0);
+      gemm(F{}, T{}, 0, F{}, F{}, nob);
+      sm(T{}, tile_k(1, 0), NS - 1, 0, T{});
     } else {
-      gemm(F{}, T{}, 0);
-      sm(F{}, tile_k(1, 0), 0, 0);
+      gemm(F{}, T{}, 0, F{}, F{}, nob);
+      sm(F{}, tile_k(1, 0), 0, 0, T{});
     }
     int j = 1;
     for (; j < nt && j + NS - 1 <= nt; ++j) {
       advance();
       tile_barrier(j);
-      gemm(T{}, T{}, j);
-      sm(T{}, tile_k(1, j), j + NS - 1, j);
+      gemm(T{}, T{}, j, F{}, F{}, nob);
+      sm(T{}, tile_k(1, j), j + NS - 1, j, T{});
     }
     for (; j < nt; ++j) {
       advance();
       tile_barrier(j);
-      gemm(T{}, T{}, j);
-      sm(F{}, tile_k(1, j), 0, j);
+      gemm(T{}, T{}, j, F{}, F{}, nob);
+      sm(F{}, tile_k(1, j), 0, j, T{});
     }
     tile_barrier(nt);
-    gemm(T{}, F{}, nt);
+    gemm(T{}, F{}, nt, F{}, F{}, nob);
   } else {  // period i: SOFTMAX_{i-1} then GEMM_i (period 0: GEMM_0 only)
+    // Group B's softmax is the longer path through a period: it reads its
+    // first GEMM operands before it, and leaves its row sums to the GEMM
+    // phase that follows (where they run in the shadow of its MFMAs).
     if constexpr (kFillB) {
       if (NS - 1 <= nt) issue(NS - 1, tile_k(NS, 0), tile_k(NS - 1, 0));
       __builtin_amdgcn_sched_barrier(0);
     }
     prefetch(0);
     lists_landed();
-    gemm(F{}, T{}, 0);
+    gemm(F{}, T{}, 0, F{}, F{}, nob);
     int j = 1;
     if constexpr (kFillB) {
       for (; j < nt && j + NS - 1 <= nt; ++j) {
@@ -576,22 +634,25 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         tile_barrier(j);
         issue(j + NS - 1, tile_k(NS, j), tile_k(NS - 1, j));
         __builtin_amdgcn_sched_barrier(0);  // the refill share ahead of the softmax arithmetic
-        sm(F{}, tile_k(0, j), 0, j);
+        const Batch pre = first_batch(j);
+        sm(F{}, tile_k(0, j), 0, j, F{});
         lists_landed();
-        gemm(T{}, T{}, j);
+        gemm(T{}, T{}, j, T{}, T{}, pre);
       }
     }
     for (; j < nt; ++j) {
       advance();
       tile_barrier(j);
-      sm(F{}, tile_k(0, j), 0, j);
+      const Batch pre = first_batch(j);
+      sm(F{}, tile_k(0, j), 0, j, F{});
       lists_landed();
-      gemm(T{}, T{}, j);
+      gemm(T{}, T{}, j, T{}, T{}, pre);
     }
     advance();
     tile_barrier(nt);
-    softmax(tile_k(0, nt));
-    gemm(T{}, F{}, nt);
+    const Batch pre = first_batch(nt);
+    softmax(tile_k(0, nt), F{});
+    gemm(T{}, F{}, nt, T{}, T{}, pre);
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16.

@@ -300,6 +300,10 @@ vidattn_status validate_fwd(Phase ph, const void* q, const void* k, const void* 
         return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps k or v");
     if (need > 0 && w < ob + qo_bytes && ob < w + (int64_t)need)
       return fail(VIDATTN_ERR_INVALID_ARG, "o overlaps the workspace");
+    // the fused calls write the workspace (pre-pass, plans) before the
+    // attention kernel reads q
+    if (ph == Phase::kFused && need > 0 && w < qb + qo_bytes && qb < w + (int64_t)need)
+      return fail(VIDATTN_ERR_INVALID_ARG, "q overlaps the workspace");
   }
   if (ph != Phase::kAttend && need > 0) {
     const char* ins[2] = {static_cast<const char*>(k), static_cast<const char*>(v)};
@@ -615,6 +619,12 @@ vidattn_status vidattn_fwd_attend_block_mask(const void* q, const uint32_t* mask
     const int64_t mask_bytes = rows * words * 4;
     const int64_t ws_bytes = (int64_t)vidattn_fwd_block_mask_workspace_size(dt, B, heads, N, d, rope != nullptr);
     if (mb < wb + ws_bytes && wb < mb + mask_bytes) return fail(VIDATTN_ERR_INVALID_ARG, "mask overlaps the workspace");
+    // the lists are written into the workspace tail before q is read
+    const char* qb = static_cast<const char*>(q);
+    const int64_t q_bytes = nbh * N * d * 2;
+    const char* tail0 = wb + vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
+    if (qb < wb + ws_bytes && tail0 < qb + q_bytes)
+      return fail(VIDATTN_ERR_INVALID_ARG, "q overlaps the list part of the workspace");
   }
   uint8_t* tail = static_cast<uint8_t*>(workspace) + vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
   int32_t* kvc = reinterpret_cast<int32_t*>(tail);

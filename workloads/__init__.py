@@ -255,3 +255,32 @@ def block_mask_words(mask) -> np.ndarray:
     bits = padded.reshape(m.shape[:-1] + (words, 32)).astype(np.uint64) << np.arange(32, dtype=np.uint64)
     return bits.sum(axis=-1).astype(np.uint32)
 
+
+
+# ---------------------------------------------------------------- planted keys (softmax edge cases)
+
+PLANT_SEED = 4242
+
+
+def planted_keys(N: int, d: int, heads: int, plants, seed: int = PLANT_SEED):
+    """Inputs whose softmax takes a chosen course: q, k, v ~ N(0,1)*0.5 and
+    every query row shifted by +1 in each component, so that a key row set to
+    c * (1, ..., 1) scores about c * d above the others (times the softmax
+    scale). ``plants`` lists, per head, (key index, c) pairs; c must be exact
+    in bf16. Keys planted with the same c are identical rows, so their logits
+    tie exactly. Returns bf16 bit patterns (1, heads, N, d) for q, k, v."""
+    out = {}
+    for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V)):
+        arr = np.empty((1, heads, N, d), dtype=np.uint16)
+        for h in range(heads):
+            g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, N, h])))
+            x = g.standard_normal((N, d), dtype=np.float32) * np.float32(0.5)
+            if name == "q":
+                x += np.float32(1.0)
+            if name == "k":
+                for j, c in plants[h]:
+                    assert float(np.float32(c)) == float(bf16_bits_to_f32(f32_to_bf16_bits(np.float32([c])))[0])
+                    x[j] = np.float32(c)
+            arr[0, h] = f32_to_bf16_bits(x)
+        out[name] = arr
+    return out["q"], out["k"], out["v"]
