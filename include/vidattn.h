@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define VIDATTN_ABI_VERSION 5
+#define VIDATTN_ABI_VERSION 6
 
 typedef enum {
   VIDATTN_OK = 0,
@@ -320,6 +320,24 @@ const char* vidattn_status_string(vidattn_status s);
  * none). The pointer stays valid until the next vidattn_* call on that
  * thread. */
 const char* vidattn_last_error(void);
+
+/* vidattn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a fixed array of
+ * VIDATTN_NOALLOC_SCRATCH_BYTES in device memory inside the library, one
+ * copy per GPU, held until the process ends; the call allocates nothing.
+ * Its first call on a device looks up that array's device address (on the
+ * current device: hip_stream must belong to it). Everything else is as for
+ * vidattn_fwd, whose results it gives bit for bit. A call whose workspace
+ * (vidattn_fwd_workspace_size) exceeds the scratch returns
+ * VIDATTN_ERR_WORKSPACE. Every call on one GPU uses the same scratch, so
+ * calls that overlap in time on one GPU (different streams, or threads)
+ * race and give wrong results: serialize them. Nothing in the scratch has to
+ * start at zero (each call rewrites what it reads). */
+#define VIDATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+vidattn_status vidattn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt,
+                                   int64_t B, int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                                   const vidattn_rope3d_desc* rope, void* hip_stream);
 
 /* VIDATTN_ABI_VERSION of the loaded library. */
 int vidattn_abi_version(void);

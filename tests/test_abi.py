@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_strings():
-    assert va.vidattn_abi_version() == 5 == va.ABI_VERSION
+    assert va.vidattn_abi_version() == 6 == va.ABI_VERSION
     for s, txt in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "workspace too small"),
                    (4, "HIP error")]:
         assert va.vidattn_status_string(s) == txt
@@ -266,7 +266,9 @@ def test_single_hip_runtime_whatever_the_import_order():
 
 def test_library_imports_no_allocation_copy_or_sync():
     """The library allocates, copies and synchronizes nothing: of the HIP
-    runtime it imports only kernel registration, launch and error strings."""
+    runtime it imports only kernel and variable registration, launch, error
+    strings, and the current device and device address of its fixed scratch
+    array (the no-allocation entry point)."""
     import shutil
     import subprocess
     nm = shutil.which("nm")
@@ -277,7 +279,7 @@ def test_library_imports_no_allocation_copy_or_sync():
     hip = sorted({line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()})
     allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
                "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipGetErrorString", "hipGetLastError",
-               "hipLaunchKernel"}
+               "hipLaunchKernel", "__hipRegisterVar", "hipGetDevice", "hipGetSymbolAddress"}
     assert set(hip) <= allowed, sorted(set(hip) - allowed)
 
 
@@ -314,3 +316,18 @@ def test_workspace_writers_reject_q_in_the_workspace():
     MK = 6 << 40
     s = va.vidattn_fwd_attend_block_mask(WSF + wsb, MK, WSF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD, need, None)
     assert s == 1 and "q overlaps the list part" in va.vidattn_last_error()
+
+
+def test_noalloc_rejects_before_any_device_work():
+    """The no-allocation entry point refuses a call whose workspace exceeds
+    its fixed scratch (naming the limit), and passes malformed arguments on
+    to vidattn_fwd's checks, all before any HIP call (these fail validation;
+    the pointers are fake)."""
+    assert va.NOALLOC_SCRATCH_BYTES == 64 << 20
+    KF, VF = QF + T // 4, QF + T // 2
+    s = va.vidattn_fwd_noalloc(QF, KF, VF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD)
+    assert s == 3 and str(64 << 20) in va.vidattn_last_error()
+    s = va.vidattn_fwd_noalloc(QF, KF, VF, OF, va.BF16, 2, 40, N5, 96, 0.1, GOOD)
+    assert s == 2 and "head dim" in va.vidattn_last_error()
+    s = va.vidattn_fwd_noalloc(None, KF, VF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD)
+    assert s == 3  # the size check comes first for this shape

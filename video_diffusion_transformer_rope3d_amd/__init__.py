@@ -21,21 +21,22 @@ __all__ = [
     "attend_block_sparse", "rope3d", "workspace_for", "SPARSE_Q_BLOCK", "SPARSE_K_BLOCK", "EXPORTED_SYMBOLS",
     "WindowDesc", "vidattn_fwd_window", "vidattn_fwd_window_workspace_size", "window_attention",
     "vidattn_fwd_attend_block_mask", "vidattn_fwd_block_mask_workspace_size", "attend_block_mask",
-    "block_mask_workspace_for",
+    "block_mask_workspace_for", "vidattn_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 BF16, F16, F32 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 SPARSE_Q_BLOCK, SPARSE_K_BLOCK = 256, 64  # VIDATTN_SPARSE_Q_BLOCK, VIDATTN_SPARSE_K_BLOCK
+NOALLOC_SCRATCH_BYTES = 64 << 20  # VIDATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED_SYMBOLS = ("vidattn_rope3d", "vidattn_rope3d_tokens", "vidattn_fwd", "vidattn_fwd_prepare",
                     "vidattn_fwd_attend",
                     "vidattn_fwd_attend_subset", "vidattn_fwd_attend_block_sparse", "vidattn_fwd_window",
                     "vidattn_fwd_window_workspace_size", "vidattn_fwd_workspace_size", "vidattn_status_string",
                     "vidattn_last_error", "vidattn_abi_version", "vidattn_fwd_attend_block_mask",
-                    "vidattn_fwd_block_mask_workspace_size")
+                    "vidattn_fwd_block_mask_workspace_size", "vidattn_fwd_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -125,6 +126,9 @@ def load() -> ctypes.CDLL:
     lib.vidattn_fwd.restype = ctypes.c_int
     lib.vidattn_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                 ctypes.POINTER(Rope3dDesc), vp, sz, vp]
+    lib.vidattn_fwd_noalloc.restype = ctypes.c_int
+    lib.vidattn_fwd_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
+                                        ctypes.POINTER(Rope3dDesc), vp]
     lib.vidattn_fwd_prepare.restype = ctypes.c_int
     lib.vidattn_fwd_prepare.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.POINTER(Rope3dDesc), vp,
                                         sz, vp]
@@ -183,6 +187,11 @@ def vidattn_fwd(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, workspace, 
     return load().vidattn_fwd(q, k, v, o, dt, B, heads, N, d, softmax_scale,
                               ctypes.byref(rope) if rope is not None else None, workspace, workspace_bytes,
                               stream)
+
+
+def vidattn_fwd_noalloc(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, stream=None) -> int:
+    return load().vidattn_fwd_noalloc(q, k, v, o, dt, B, heads, N, d, softmax_scale,
+                                      ctypes.byref(rope) if rope is not None else None, stream)
 
 
 def vidattn_fwd_prepare(k, v, dt, B, heads, N, d, rope, workspace, workspace_bytes, stream=None) -> int:

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "vidattn.h"
@@ -640,6 +641,61 @@ vidattn_status vidattn_fwd_attend_block_mask(const void* q, const uint32_t* mask
   x.maxb = (int)nkt;
   if (vidattn_status s = launch_attend(q, q, q, workspace, o, dt, nbh, N, d, softmax_scale, rp, st, x)) return s;
   return ok();
+}
+
+}  // extern "C"
+
+
+// ---------------------------------------------------------------- fixed scratch (no allocation)
+
+// The workspace of vidattn_fwd_noalloc: a fixed array in device memory, one
+// copy per GPU the library runs on, held until the process ends. In host
+// code its name stands for a host-side shadow, not a device address; the
+// device address is looked up once per device (hipGetSymbolAddress) and
+// only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[VIDATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up once per device).
+vidattn_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(VIDATTN_ERR_HIP, "no usable current HIP device (%d)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(VIDATTN_ERR_HIP, "device address of the fixed scratch: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VIDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vidattn_status vidattn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,
+                                   int64_t heads, int64_t N, int64_t d, float softmax_scale,
+                                   const vidattn_rope3d_desc* rope, void* hip_stream) {
+  // 0 for arguments vidattn_fwd rejects by dtype or size: it reports them
+  const size_t need = vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
+  if (need > (size_t)VIDATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(VIDATTN_ERR_WORKSPACE,
+                "this call needs %zu bytes of workspace; the fixed scratch of vidattn_fwd_noalloc holds %zu "
+                "(use vidattn_fwd with a caller workspace)",
+                need, (size_t)VIDATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0)
+    if (vidattn_status s = scratch_address(&ws)) return s;
+  return vidattn_fwd(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, ws, need, hip_stream);
 }
 
 }  // extern "C"
