@@ -294,6 +294,35 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     }
     return (part[0] + part[1]) + (part[2] + part[3]);
   };
+  // The exact step's rescale: the tile's exact maximum (relative to the
+  // current m) becomes part of m; a row that has seen no visible key yet
+  // takes the tile's maximum as its m (and keeps m = 0 if the tile shows it
+  // none). O is scaled, the scores are moved to the new m; returns alpha,
+  // the factor l must be scaled by.
+  auto rescale_to_tile_max = [&]() __attribute__((always_inline)) {
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = xor32_max(mx) + kBias;
+    const bool seen = mx > -INFINITY;
+    const float delta = !m_valid ? (seen ? mx : 0.f) : fmaxf(mx, 0.f);
+    const float alpha = !m_valid ? 1.f : __builtin_amdgcn_exp2f(-delta);
+    m_valid = m_valid || seen;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    m += delta;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = -(m + kBias);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] -= delta;
+    return alpha;
+  };
 
   constexpr int kWaitNewer = STAGE_LOADS * (NS - 2);
   constexpr int kVmcntNewer = (kWaitNewer & 0xF) | ((kWaitNewer >> 4) << 14) | (0x7 << 4) | (0xF << 8);
@@ -455,6 +484,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     constexpr int NK = decltype(SC)::value ? 2 * KSTEPS : 0;  // K operand blocks
     constexpr int NOP = NV + NK;
     static_assert(NOP % RB == 0, "operand batches");
+    constexpr int NB = NOP / RB;
+    // scheduling groups that keep the batch structure of batches b0 .. b1:
+    // the reads of batch b + 1, then the MFMAs of batch b
+    auto groups = [&](int b0, int b1) __attribute__((always_inline)) {
+      for (int b = b0; b <= b1; ++b) {
+        if (b + 1 < NB) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);                // MFMA
+      }
+    };
     // operand i < NV: V block (db, ms) = i; else K block (kb, s) = i - NV
     auto addr = [&](int i) __attribute__((always_inline)) { return st + (i < NV ? TILE + i * 1024 : (i - NV) * 1024); };
     // accumulator input of the first score MFMA per key block: -m, or -inf
@@ -497,65 +535,38 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       }
     }
     if constexpr (decltype(SUM)::value) l += rowsum();
-    // keep the batch structure: RB reads up front, then (RB reads, RB MFMAs) per batch
-#pragma unroll
-    for (int b = 0; b < NOP / RB; ++b) {
-      if (b > 0 || !decltype(PRE)::value) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
-      if (b > 0) __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);  // MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+    // keep the batch structure: the first RB reads up front (unless read
+    // ahead), then per batch the next RB reads and this batch's RB MFMAs
+    if constexpr (!decltype(PRE)::value) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);
+    groups(0, NB - 1);
   };
 
-  // SOFTMAX phase of the scores of workspace tile t (in the last tile, keys
-  // past N get -inf).
-  // SUM: add the row sums to l here (else the next GEMM phase does).
-  auto softmax = [&](int t, auto SUM) __attribute__((always_inline)) {
-    {
-      if (tail < KT && t == nkt - 1) {
+  // In the last key tile, keys past N get -inf.
+  auto tail_mask = [&](int t) __attribute__((always_inline)) {
+    if (tail < KT && t == nkt - 1) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
-            if (key >= tail) sacc[kb][i] = -INFINITY;
-          }
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
+          if (key >= tail) sacc[kb][i] = -INFINITY;
+        }
     }
+  };
+  // SOFTMAX phase of the scores of workspace tile t. SUM: add the row sums
+  // to l here (else the next GEMM phase does).
+  auto softmax = [&](int t, auto SUM) __attribute__((always_inline)) {
+    tail_mask(t);
     const bool big = (probs() & 0x40004000u) != 0u;  // some p >= 2 (or not finite)
     // the exact step: for a row's first tile with a visible key (a row with
     // no visible key in this tile keeps m unset), and when a score lies more
     // than kBias + 1 above m
     if (__builtin_amdgcn_ballot_w64((!m_valid && wvis != 0u) || big) != 0) {
-      // exact maximum of the tile (relative to the current m); a row that
-      // has seen no visible key yet takes the tile's maximum as its m (and
-      // keeps m = 0 if the tile shows it none)
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = xor32_max(mx) + kBias;
-      const bool seen = mx > -INFINITY;
-      const float delta = !m_valid ? (seen ? mx : 0.f) : fmaxf(mx, 0.f);
-      const float alpha = !m_valid ? 1.f : __builtin_amdgcn_exp2f(-delta);
-      m_valid = m_valid || seen;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      m += delta;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) negm[i] = -(m + kBias);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] -= delta;
+      l *= rescale_to_tile_max();
       probs();
     }
     if constexpr (decltype(SUM)::value) l += rowsum();
   };
-
   using T = std::true_type;
   using F = std::false_type;
   // One barrier per tile period i; within it group A runs GEMM_i then
@@ -628,25 +639,25 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     lists_landed();
     gemm(F{}, T{}, 0, F{}, F{}, nob);
     int j = 1;
+    auto period_b = [&](int jj) __attribute__((always_inline)) {
+      const Batch pre = first_batch(jj);
+      sm(F{}, tile_k(0, jj), 0, jj, F{});
+      lists_landed();
+      gemm(T{}, T{}, jj, T{}, T{}, pre);
+    };
     if constexpr (kFillB) {
       for (; j < nt && j + NS - 1 <= nt; ++j) {
         advance();
         tile_barrier(j);
         issue(j + NS - 1, tile_k(NS, j), tile_k(NS - 1, j));
         __builtin_amdgcn_sched_barrier(0);  // the refill share ahead of the softmax arithmetic
-        const Batch pre = first_batch(j);
-        sm(F{}, tile_k(0, j), 0, j, F{});
-        lists_landed();
-        gemm(T{}, T{}, j, T{}, T{}, pre);
+        period_b(j);
       }
     }
     for (; j < nt; ++j) {
       advance();
       tile_barrier(j);
-      const Batch pre = first_batch(j);
-      sm(F{}, tile_k(0, j), 0, j, F{});
-      lists_landed();
-      gemm(T{}, T{}, j, T{}, T{}, pre);
+      period_b(j);
     }
     advance();
     tile_barrier(nt);
