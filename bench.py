@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s on 1 MI355X and % of bf16 MFMA peak; ms per DiT attention call"
 PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
-PROFILE_GLOB = os.path.join(ROOT, "profiles", "*traffic*.md")
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 KERNEL = "attn_fwd_bf16_pp_kernel"
 
 
@@ -44,74 +44,104 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_counters(workload_name: str) -> dict:
-    """Matrix-core busy fraction and clock of the attention kernel from a
-    committed rocprofv3 counter summary, if it was taken on the current
-    kernel source and workload."""
+def committed_summary(pattern: str, workload_name: str, kernel: str, keys) -> dict | None:
+    """Figures from a committed rocprofv3 summary under profiles/ (file name
+    matching ``pattern``) taken on the current kernel source, this workload
+    and this kernel: the file, the kernel's duration in that profiled run
+    (``kernel_ms``) and the requested keys; None if there is none."""
     src = kernel_source_hash()
-    for p in glob.glob(os.path.join(ROOT, "profiles", "*counters*.md")):
+    for p in sorted(glob.glob(os.path.join(ROOT, "profiles", pattern))):
         text = open(p).read()
-        m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
-        m_wl = re.search(r"workload:\s*(\S+)", text)
-        if not (m_src and m_wl and m_src.group(1) == src and m_wl.group(1) == workload_name):
+
+        def field(k):
+            m = re.search(r"(?:^|\n)-?\s*" + re.escape(k) + r":\s*(\S+)", text)
+            return m.group(1) if m else None
+
+        if field("kernel_source_sha256") != src or field("workload") != workload_name:
             continue
-        out = {}
-        for key in ("mfma_busy_frac", "clock_ghz"):
-            m = re.search(key + r":\s*([0-9.eE+]+)", text)
-            if m:
-                out[key] = float(m.group(1))
+        if field("kernel") not in (None, kernel):
+            continue
+        out = {"file": os.path.relpath(p, ROOT)}
+        for k in ("kernel_ms", *keys):
+            v = field(k)
+            if v is not None:
+                out[k] = float(v)
         return out
-    return {}
-
-
-def committed_traffic(workload_name: str):
-    """HBM bytes per attention launch from a committed rocprofv3 counter
-    summary, if it was taken on the current kernel source and workload."""
-    src = kernel_source_hash()
-    for p in glob.glob(PROFILE_GLOB):
-        text = open(p).read()
-        m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
-        m_wl = re.search(r"workload:\s*(\S+)", text)
-        m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-        if m_src and m_b and m_wl and m_src.group(1) == src and m_wl.group(1) == workload_name:
-            return float(m_b.group(1))
     return None
+
+
+def profile_block(workload_name: str, kernel: str, kernel_ms: float) -> tuple:
+    """(traffic bytes per launch or None, the 'profile' block of the roofline):
+    counters of separate rocprofv3 runs on the same kernel source, labelled
+    with their file and the kernel time in those runs, which may have been on
+    another board (boards of this GPU differ by several per cent)."""
+    tr = committed_summary("*traffic*.md", workload_name, kernel, ("traffic_bytes_per_launch",))
+    ct = committed_summary("*counters*.md", workload_name, kernel, ("mfma_busy_frac", "clock_ghz"))
+    block = {}
+    traffic = None
+    if tr and "traffic_bytes_per_launch" in tr:
+        traffic = tr["traffic_bytes_per_launch"]
+        block["traffic_file"] = tr["file"]
+        if "kernel_ms" in tr:
+            block["traffic_run_kernel_ms"] = tr["kernel_ms"]
+    if ct:
+        block["counters_file"] = ct["file"]
+        for k in ("kernel_ms", "mfma_busy_frac", "clock_ghz"):
+            if k in ct:
+                block[{"kernel_ms": "counters_run_kernel_ms"}.get(k, k)] = ct[k]
+    if block:
+        block["this_run_kernel_ms"] = round(kernel_ms, 3)
+        block["note"] = ("counters from separate rocprofv3 runs of the same kernel source (files above); "
+                         "achieved and frac are this run's")
+    return traffic, (block or None)
 
 
 def cpu_baseline(wl, host, budget_s: float):
     """The oracle as it stands, on sampled query rows of whole (b, head)
-    slices (every key), for about ``budget_s`` seconds of host time."""
+    slices (every key), for about ``budget_s`` seconds of wall time: the
+    slices are spread over a pool of one worker per host core (up to 16),
+    each running the oracle with a single BLAS thread."""
     import numpy as np
     import oracle
     import workloads as wlmod
-    from threadpoolctl import threadpool_info
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
 
     cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, cores))
     dec = oracle.decode_bf16 if wl.dtype == "bf16" else (lambda a: a.astype(np.float64))
-    slices, rows_total, t_total = 0, 0, 0.0
     pairs = [(b, h) for b in range(wl.B) for h in range(wl.heads)]
-    for (b, h) in pairs:
+
+    def one(bh):
+        b, h = bh
         rows = wlmod.sample_rows(wl, b, h)
         q, k, v = (dec(host[n][b, h]) for n in ("q", "k", "v"))
-        t0 = time.perf_counter()
         oracle.rope_attention(q, k, v, wl.grid, wl.split, wl.theta, wl.scale, rows=rows)
-        t_total += time.perf_counter() - t0
-        slices += 1
-        rows_total += rows.size
-        if t_total >= budget_s:
-            break
+        return rows.size
+
+    rows_total, slices = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        for w0 in range(0, len(pairs), workers):
+            rows_total += sum(ex.map(one, pairs[w0:w0 + workers]))
+            slices += len(pairs[w0:w0 + workers])
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    wall = time.perf_counter() - t0
     flops = 4.0 * rows_total * wl.N * wl.d
-    blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
     return {
-        "value": flops / t_total / 1e12,
+        "value": flops / wall / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas[0]) if blas else cores,
+        "cores": workers,
         "kind": "oracle",
         "sample": f"{slices} (b, head) slices x {rows_total // max(slices, 1)} sampled query rows against all "
-                  f"{wl.N} keys (fp64 NumPy, keys rotated in full per slice); {t_total:.1f} s; "
-                  f"{cores} host cores available",
-        "seconds": t_total,
-        "ms_per_call_extrapolated": t_total / rows_total * wl.N * wl.B * wl.heads * 1e3,
+                  f"{wl.N} keys (fp64 NumPy, keys rotated in full per slice), {workers} slices at a time on "
+                  f"{workers} worker threads with 1 BLAS thread each; {wall:.1f} s wall; {cores} host cores "
+                  f"available",
+        "workers": workers,
+        "blas_threads_per_worker": 1,
+        "seconds": wall,
+        "ms_per_call_extrapolated": wall / rows_total * wl.N * wl.B * wl.heads * 1e3,
     }
 
 
@@ -152,10 +182,12 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="host time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--variant", choices=("dense", "subset", "sparse", "window"), default="dense",
+    ap.add_argument("--variant", choices=("dense", "subset", "sparse", "window", "rope3d", "prepass"),
+                    default="dense",
                     help="subset: a quarter of the query tokens attend to all keys; sparse: block-sparse lists "
                          "(a band of 96 key blocks each side of the query block plus 96 global key blocks); "
-                         "window: local window of radius (1, 7, 7) around each query")
+                         "window: local window of radius (1, 7, 7) around each query; rope3d: the standalone "
+                         "rotation of Q (bf16 to bf16); prepass: the key/value pre-pass alone (both HBM-bound)")
     ap.add_argument("--no-gemm-context", action="store_true",
                     help="skip the same-box torch.mm bf16 reference rate reported after the timed region")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -257,13 +289,15 @@ def main() -> int:
                         "min": round(min(per_call), 3)},
         "breakdown_ms": {"kv_prepass": round(statistics.mean(prep_ms), 3), "attention_kernel": round(attn_mean, 3)},
         "roofline": {"kernel": KERNEL, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": committed_traffic(wl.name)},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
     }
     # counter-derived figures (committed rocprofv3 summaries of this kernel source, else absent)
-    if result["roofline"]["traffic"] is not None:
-        result["roofline"]["hbm_gb_s"] = round(result["roofline"]["traffic"] / (attn_mean * 1e-3) / 1e9, 1)
-    result["roofline"].update(committed_counters(wl.name))
+    traffic, prof = profile_block(wl.name, KERNEL, attn_mean)
+    result["roofline"]["traffic"] = traffic
+    if traffic is not None:
+        result["roofline"]["hbm_gb_s"] = round(traffic / (attn_mean * 1e-3) / 1e9, 1)
+    if prof:
+        result["roofline"]["profile"] = prof
 
     if not args.no_gemm_context:
         result["gemm_context"] = gemm_context(dev, achieved)
@@ -293,6 +327,8 @@ def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
     import workloads as wlmod
 
     QB, KB = va.SPARSE_Q_BLOCK, va.SPARSE_K_BLOCK
+    if args.variant in ("rope3d", "prepass"):
+        return hbm_bench(args, va, wl, q, k, v, ws, rope, stream)
     if args.variant == "window":
         return window_bench(args, va, wl, host, q, k, v, rope, stream)
     if args.variant == "subset":
@@ -400,6 +436,54 @@ def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
     return 0
 
 
+def hbm_bench(args, va, wl, q, k, v, ws, rope, stream) -> int:
+    """One of the two HBM-bound kernels alone, at the workload's shape: the
+    standalone rotation of Q (reads and writes B*heads*N*d bf16 values) or
+    the key/value pre-pass (reads K and V, writes the fp16 rotated keys and
+    the transposed V into the workspace). GB/s of algorithmic bytes against
+    the 8 TB/s HBM peak."""
+    import torch
+
+    n_el = wl.B * wl.heads * wl.N * wl.d
+    if args.variant == "rope3d":
+        out = torch.empty_like(q)
+        call = lambda: va.rope3d(q, wl.grid, wl.split, wl.theta, out=out, stream=stream)  # noqa: E731
+        nbytes = 2.0 * n_el * 2
+        kernel = "rope3d_kernel"
+        what = "standalone rotation of Q, bf16 in, bf16 out"
+    else:
+        call = lambda: va.prepare(k, v, workspace=ws, stream=stream, **rope)  # noqa: E731
+        nbytes = 2.0 * n_el * 2 + ws.numel()
+        kernel = "prep_kv_kernel"
+        what = "key/value pre-pass: K and V read, rotated fp16 keys and transposed V written"
+    for _ in range(max(args.warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in es:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = statistics.mean(a.elapsed_time(b) for a, b in es)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": f"{kernel} GB/s on 1 MI355X and % of HBM peak", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {**wl.describe(), "workload": f"{wl.name}-{args.variant}", "variant": args.variant,
+                   "bytes_per_call": nbytes, "what": what},
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    traffic, prof = profile_block(result["config"]["workload"], kernel, ms)
+    result["roofline"]["traffic"] = traffic
+    if prof:
+        result["roofline"]["profile"] = prof
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def window_plan_lists(wl, radius):
     """The 64-key tiles the window attention's plan lists for each 256-query
     block, ascending (the planning rule restated: every row within r_h of a
@@ -458,8 +542,10 @@ def window_tiles(wl, radius):
 
 def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
     """Local-window attention of radius (1, 7, 7): a call is pre-pass + plan
-    + attention; FLOPs count the query-key pairs of the visited tiles (the
-    roofline) and, apart, the pairs inside the windows."""
+    + attention. The value counts the method's own work, the query-key pairs
+    inside the windows; the pairs of the visited 64-key tiles (what the
+    matrix cores compute) are reported beside it, for the whole call and for
+    the attention kernel alone (timed on its own from the same workspace)."""
     import numpy as np
     import torch
 
@@ -469,6 +555,7 @@ def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
     radius = (1, 7, 7)
     visited, inside = window_tiles(wl, radius)
     flops = 4.0 * wl.B * wl.heads * visited * wl.d
+    flops_in = 4.0 * wl.B * wl.heads * inside * wl.d
     n = va.vidattn_fwd_window_workspace_size(va.BF16, wl.B, wl.heads, wl.N, wl.d, True)
     wws = torch.empty(n, dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
@@ -492,17 +579,23 @@ def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
         b.record(stream)
     torch.cuda.synchronize()
     ms = statistics.mean(a.elapsed_time(b) for a, b in es)
+    tflops = lambda f, t: f / (t * 1e-3) / 1e12  # noqa: E731
     result = {
-        "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(tflops(flops_in, ms), 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {**wl.describe(), "workload": f"{wl.name}-window-r{radius[0]}{radius[1]}{radius[2]}",
-                   "variant": "window", "radius": list(radius), "flops_per_call": flops,
+                   "variant": "window", "radius": list(radius), "flops_per_call": flops_in,
+                   "flops_per_call_visited_tiles": flops,
                    "visited_fraction": round(visited / wl.N ** 2, 4),
                    "pairs_inside_windows_fraction": round(inside / wl.N ** 2, 5)},
-        "roofline": {"kernel": KERNEL, "bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 2),
-                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
-                     "traffic": None, "note": "whole call (pre-pass + plan + attention) against visited-tile FLOPs"},
+        "roofline": {"kernel": KERNEL, "bound": "mfma", "achieved": round(tflops(flops_in, ms), 2),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops(flops_in, ms) / PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "note": "whole call (pre-pass + plan + attention) against the FLOPs of the pairs inside the "
+                             "windows; visited_* count every pair of the visited 64-key tiles",
+                     "visited_achieved": round(tflops(flops, ms), 2),
+                     "visited_frac": round(tflops(flops, ms) / PEAK_TFLOPS, 4)},
     }
     if not args.no_parity:
         from threadpoolctl import threadpool_limits
