@@ -466,12 +466,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // The first operand batch of a GEMM phase with the P.V product (V blocks
   // 0 .. RB-1). Group B reads it right after the barrier, ahead of its
   // softmax, so that its GEMM phase starts without an LDS wait.
+  auto vb = [&](int i) __attribute__((always_inline)) { return (i % DB) * MS + i / DB; };
   auto first_batch = [&](int jj) __attribute__((always_inline)) {
     const uint8_t* st = stage_ptr(jj);
     Batch b;
     b.st = st;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) b.v[r] = *reinterpret_cast<const u32x4*>(st + TILE + r * 1024);
+    for (int r = 0; r < RB; ++r)
+      b.v[r] = *reinterpret_cast<const u32x4*>(st + TILE + vb(r) * 1024);
     __builtin_amdgcn_sched_barrier(0);  // issue the reads before what follows
     return b;
   };
@@ -493,8 +495,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);                // MFMA
       }
     };
-    // operand i < NV: V block (db, ms) = i; else K block (kb, s) = i - NV
-    auto addr = [&](int i) __attribute__((always_inline)) { return st + (i < NV ? TILE + i * 1024 : (i - NV) * 1024); };
+    // Operand i < NV is V block vb(i) = (db, ms), else K block kbs(i - NV) =
+    // (kb, s). Consecutive MFMAs share their register operand (P block ms
+    // for DB products, Q step s for the two key blocks) and write different
+    // accumulators; each accumulator still sums in the same order.
+    auto kbs = [&](int i) __attribute__((always_inline)) { return (i % 2) * KSTEPS + i / 2; };
+    auto addr = [&](int i) __attribute__((always_inline)) {
+      return st + (i < NV ? TILE + vb(i) * 1024 : kbs(i - NV) * 1024);
+    };
     // accumulator input of the first score MFMA per key block: -m, or -inf
     // for a key outside the window (sign-extended bit, then a bit select)
     f32x16 cneg[2];
@@ -525,10 +533,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         const int i = b * RB + r;
         const u32x4 a = buf[b & 1][r];
         if (i < NV) {
-          const int db = i / MS, ms = i % MS;
+          const int db = vb(i) / MS, ms = vb(i) % MS;
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pk[ms], oacc[db], 0, 0, 0);
         } else {
-          const int kb = (i - NV) / KSTEPS, s = (i - NV) % KSTEPS;
+          const int kb = kbs(i - NV) / KSTEPS, s = kbs(i - NV) % KSTEPS;
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), qreg[s],
                                                             s == 0 ? (WIN ? cneg[kb] : negm) : sacc[kb], 0, 0, 0);
         }
