@@ -379,6 +379,12 @@ WINDOW_CASES = [
     ((2, 4, 70), 64, (16, 24, 24), 2, 1, (0, 2, 9)),
     ((3, 2, 100), 128, (44, 42, 42), 1, 2, (1, 0, 30)),
     ((2, 3, 129), 128, (44, 42, 42), 1, 1, (1, 1, 200)),
+    # per-workgroup cos/sin table: too large for a ring stage (each lane
+    # evaluates its angles), for d = 128 and d = 64, and a split with empty
+    # frame and column chunks
+    ((1, 2, 400), 128, (44, 42, 42), 1, 1, (0, 1, 20)),
+    ((1, 2, 200), 64, (16, 24, 24), 1, 2, (0, 1, 9)),
+    ((3, 11, 17), 128, (0, 128, 0), 1, 2, (1, 2, 3)),
 ]
 
 

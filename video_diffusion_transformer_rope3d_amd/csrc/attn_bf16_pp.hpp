@@ -189,6 +189,38 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     const int cf = rp.enabled ? pos / hw : 0;
     const int cy = rp.enabled ? (pos - cf * hw) / rp.W : 0;
     const int cx = pos - cf * hw - cy * rp.W;
+    // Window variant: the cos/sin of every (axis position, pair) of the
+    // grid, once per workgroup, in the ring stage the prologue does not fill
+    // (stage NS-1, first refilled after the barrier that opens tile period
+    // 0): per axis, extent x pairs entries of (cos, sin), t then h then w.
+    // The 256 rows of a workgroup share few positions per axis, so this
+    // evaluates far fewer angles than one per (row, pair), which matters
+    // where a workgroup visits few tiles; the values are those of
+    // rope_angle_cos_sin, so the rotation is the same bit for bit. Grids
+    // whose table does not fit the stage evaluate each lane's angles.
+    const int npt = rp.pair_t, nph = rp.pair_th - rp.pair_t, npw = D / 2 - rp.pair_th;
+    const int base_h = rp.F * npt, base_w = base_h + rp.H * nph, n_ent = base_w + rp.W * npw;
+    const bool table = WIN && NS >= 3 && rp.enabled && n_ent <= STAGE / 8;
+    float2* tbl = reinterpret_cast<float2*>(lds + (NS - 1) * STAGE);
+    if (table) {
+      for (int e = threadIdx.x; e < n_ent; e += NW * 64) {
+        int apos, pair;
+        if (e < base_h) {
+          apos = e / npt;
+          pair = e - apos * npt;
+        } else if (e < base_w) {
+          apos = (e - base_h) / nph;
+          pair = rp.pair_t + (e - base_h - apos * nph);
+        } else {
+          apos = (e - base_w) / npw;
+          pair = rp.pair_th + (e - base_w - apos * npw);
+        }
+        float c, sn;
+        rope_angle_cos_sin(apos, rp.omega[pair], c, sn);
+        tbl[e] = float2{c, sn};
+      }
+      lds_barrier();
+    }
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       float x[8];
@@ -199,11 +231,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           // pair 8s + 4g + j: both candidates (g = 0, 1) are wave-uniform
           // kernel arguments, read once into scalar registers
           const int p0 = 8 * s + j, p1 = p0 + 4;
-          const double w0 = uniform_f64(rp.omega[p0]), w1 = uniform_f64(rp.omega[p1]);
-          const int a0 = p0 < rp.pair_t ? cf : (p0 < rp.pair_th ? cy : cx);
-          const int a1 = p1 < rp.pair_t ? cf : (p1 < rp.pair_th ? cy : cx);
           float c, sn;
-          rope_angle_cos_sin(g ? a1 : a0, g ? w1 : w0, c, sn);
+          if (table) {
+            const int p = g ? p1 : p0;
+            const int e = p < rp.pair_t ? cf * npt + p
+                                        : (p < rp.pair_th ? base_h + cy * nph + (p - rp.pair_t)
+                                                          : base_w + cx * npw + (p - rp.pair_th));
+            const float2 cs = tbl[e];
+            c = cs.x;
+            sn = cs.y;
+          } else {
+            const double w0 = uniform_f64(rp.omega[p0]), w1 = uniform_f64(rp.omega[p1]);
+            const int a0 = p0 < rp.pair_t ? cf : (p0 < rp.pair_th ? cy : cx);
+            const int a1 = p1 < rp.pair_t ? cf : (p1 < rp.pair_th ? cy : cx);
+            rope_angle_cos_sin(g ? a1 : a0, g ? w1 : w0, c, sn);
+          }
           rotate_pair(x[2 * j], x[2 * j + 1], c, sn);
         }
       }
