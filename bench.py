@@ -188,6 +188,8 @@ def main() -> int:
                          "(a band of 96 key blocks each side of the query block plus 96 global key blocks); "
                          "window: local window of radius (1, 7, 7) around each query; rope3d: the standalone "
                          "rotation of Q (bf16 to bf16); prepass: the key/value pre-pass alone (both HBM-bound)")
+    ap.add_argument("--window-layout", choices=("auto", "rows", "patches"), default="auto",
+                    help="tiling of the window variant (auto: the one that visits fewer key tiles)")
     ap.add_argument("--no-gemm-context", action="store_true",
                     help="skip the same-box torch.mm bf16 reference rate reported after the timed region")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -523,18 +525,61 @@ def window_plan_lists(wl, radius):
     return lists
 
 
-def window_plan_counts(wl, radius):
-    return [len(t) for t in window_plan_lists(wl, radius)]
-
-
-def window_tiles(wl, radius):
-    """Query-key pairs the window attention visits (the tiles its plan lists
-    per 256-query block, times the block's rows) and the pairs inside the
-    windows."""
+def window_patch_lists(wl, radius):
+    """The patch layout's plan restated: for each 16 x 16 query patch
+    (f, py, px) of one frame, frame-major, every 8 x 8 key patch
+    (tf, ty, tx), tile index (tf*ceil(H/8) + ty)*ceil(W/8) + tx, of frames
+    within r_f whose rows and columns meet the patch's rows and columns
+    widened by r_h and r_w (clipped to the grid), ascending."""
     F, H, W = wl.grid
-    N = wl.N
+    rf, rh, rw = (min(r, n) for r, n in zip(radius, wl.grid))
+    tyn, txn = -(-H // 8), -(-W // 8)
+
+    def span(p, n, r):
+        return max(0, 16 * p - r) // 8, min(n - 1, min(16 * p + 15, n - 1) + r) // 8
+
+    lists = []
+    for f in range(F):
+        for py in range(-(-H // 16)):
+            for px in range(-(-W // 16)):
+                (y0, y1), (x0, x1) = span(py, H, rh), span(px, W, rw)
+                lists.append([(tf * tyn + ty) * txn + tx for tf in range(max(0, f - rf), min(F - 1, f + rf) + 1)
+                              for ty in range(y0, y1 + 1) for tx in range(x0, x1 + 1)])
+    return lists
+
+
+def window_layout(wl, radius):
+    """The layout the library picks for this window: patches when they list
+    fewer key tiles in all (ties: rows)."""
+    F, H, W = wl.grid
+    if F * -(-H // 8) * -(-W // 8) >= 1 << 22 or F * -(-H // 16) * -(-W // 16) >= 1 << 22:
+        return "rows"
+    rows = sum(len(t) for t in window_plan_lists(wl, radius))
+    patches = sum(len(t) for t in window_patch_lists(wl, radius))
+    return "patches" if patches < rows else "rows"
+
+
+def window_plan_counts(wl, radius, layout="rows"):
+    lists = window_patch_lists(wl, radius) if layout == "patches" else window_plan_lists(wl, radius)
+    return [len(t) for t in lists]
+
+
+def window_block_rows(wl, layout):
+    """Grid tokens (real query rows) of each query block of the layout."""
+    F, H, W = wl.grid
+    if layout == "rows":
+        return [min(wl.N, 256 * i + 256) - 256 * i for i in range(-(-wl.N // 256))]
+    return [(min(H, 16 * py + 16) - 16 * py) * (min(W, 16 * px + 16) - 16 * px)
+            for _ in range(F) for py in range(-(-H // 16)) for px in range(-(-W // 16))]
+
+
+def window_tiles(wl, radius, layout="rows"):
+    """Query-key pairs the window attention visits (the tiles its plan lists
+    per query block, times the block's real query rows) and the pairs inside
+    the windows."""
+    F, H, W = wl.grid
     rf, rh, rw = radius
-    visited = sum(c * 64 * (min(N, 256 * i + 256) - 256 * i) for i, c in enumerate(window_plan_counts(wl, radius)))
+    visited = sum(c * 64 * r for c, r in zip(window_plan_counts(wl, radius, layout), window_block_rows(wl, layout)))
     ext = lambda n, r: sum(min(n - 1, c + r) - max(0, c - r) + 1 for c in range(n))
     inside = ext(F, rf) * ext(H, rh) * ext(W, rw)
     return visited, inside
@@ -553,24 +598,31 @@ def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
     import workloads as wlmod
 
     radius = (1, 7, 7)
-    visited, inside = window_tiles(wl, radius)
+    layout = args.window_layout if args.window_layout != "auto" else window_layout(wl, radius)
+    visited, inside = window_tiles(wl, radius, layout)
     flops = 4.0 * wl.B * wl.heads * visited * wl.d
     flops_in = 4.0 * wl.B * wl.heads * inside * wl.d
-    n = va.vidattn_fwd_window_workspace_size(va.BF16, wl.B, wl.heads, wl.N, wl.d, True)
+    desc = va.WindowDesc.make(wl.grid, radius, args.window_layout)
+    n = va.vidattn_fwd_window_workspace_size(va.BF16, wl.B, wl.heads, wl.N, wl.d, True, desc)
     wws = torch.empty(n, dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
     call = lambda: va.window_attention(q, k, v, radius, grid=wl.grid, split=wl.split, theta=wl.theta,
-                                       scale=wl.scale, workspace=wws, out=o, stream=stream)
+                                       scale=wl.scale, layout=args.window_layout, workspace=wws, out=o,
+                                       stream=stream)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
     # the FLOP count above restates the planning rule: check it against the
     # tile counts the planning kernel wrote (the workspace tail starts with them)
-    base = va.vidattn_fwd_workspace_size(va.BF16, wl.B, wl.heads, wl.N, wl.d, True)
-    nqb = -(-wl.N // 256)
+    want = window_plan_counts(wl, radius, layout)
+    nqb = len(want)
+    nkt = (wl.N + 63) // 64 if layout == "rows" else wl.grid[0] * -(-wl.grid[1] // 8) * -(-wl.grid[2] // 8)
+    base = 256 * wl.d * wl.B * wl.heads * nkt  # the key/value image comes first
+    if n != base + (4 * nqb + 255) // 256 * 256 + 4 * nqb * nkt:
+        raise RuntimeError(f"window workspace size does not match the {layout} layout")
     if args.warmup > 0:
         got = wws[base:base + 4 * nqb].view(torch.int32).cpu().tolist()
-        if got != window_plan_counts(wl, radius):
+        if got != want:
             raise RuntimeError("window plan tile counts differ from the FLOP-count rule")
     es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in es:
@@ -585,7 +637,7 @@ def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {**wl.describe(), "workload": f"{wl.name}-window-r{radius[0]}{radius[1]}{radius[2]}",
-                   "variant": "window", "radius": list(radius), "flops_per_call": flops_in,
+                   "variant": "window", "radius": list(radius), "layout": layout, "flops_per_call": flops_in,
                    "flops_per_call_visited_tiles": flops,
                    "visited_fraction": round(visited / wl.N ** 2, 4),
                    "pairs_inside_windows_fraction": round(inside / wl.N ** 2, 5)},

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define VIDATTN_ABI_VERSION 6
+#define VIDATTN_ABI_VERSION 7
 
 typedef enum {
   VIDATTN_OK = 0,
@@ -242,11 +242,27 @@ vidattn_status vidattn_fwd_attend_block_sparse(const void* q, const void* worksp
  * attends to the keys (f', y', x') with |f - f'| <= r_f, |y - y'| <= r_h and
  * |x - x'| <= r_w (a centred box, clipped at the grid border; every query
  * sees at least itself). F, H, W as in vidattn_rope3d_desc (F*H*W == N);
- * radii >= 0, and a radius at or beyond its extent reaches the whole axis. */
+ * radii >= 0, and a radius at or beyond its extent reaches the whole axis.
+ * layout picks how the attention tiles queries and keys; it changes the work
+ * done, never the result beyond rounding order (the keys of a query are
+ * summed in another order):
+ *   VIDATTN_WINDOW_AUTO     the layout that visits fewer key tiles (ties:
+ *                           rows), computed on the host from the grid and
+ *                           radii;
+ *   VIDATTN_WINDOW_ROWS     blocks of 256 consecutive queries, tiles of 64
+ *                           consecutive keys, whole grid rows listed;
+ *   VIDATTN_WINDOW_PATCHES  16 x 16 query patches and 8 x 8 key patches of
+ *                           one frame (unsupported when the grid has 2^22 or
+ *                           more key patches or query patches). */
 typedef struct {
   int64_t F, H, W;
   int32_t r_f, r_h, r_w;
+  int32_t layout;
 } vidattn_window_desc;
+
+#define VIDATTN_WINDOW_AUTO 0
+#define VIDATTN_WINDOW_ROWS 1
+#define VIDATTN_WINDOW_PATCHES 2
 
 /* Block-sparse attention driven by a bit mask, the form of ScalingAttention's
  * bit-wise block-sparse kernel (a per-head block mask; its abstract on the
@@ -284,26 +300,31 @@ size_t vidattn_fwd_block_mask_workspace_size(vidattn_dtype dt, int64_t B, int64_
  * "3D RoPE, 3D VAEs, and flash attention") and the sliding local windows of
  * Sparse Forcing (its abstract on thelatestinai.com/papers/2609.18077); the
  * pages fix no window shape, the centred box above is the plainest reading.
- * One call runs the key/value pre-pass, a planning kernel that lists per
- * 256-query block the 64-key tiles of the grid rows its queries' windows
- * reach (in the workspace), and the attention over those tiles with the keys
- * outside each query's box masked. Arguments as for vidattn_fwd, plus:
- *   window     non-null; its grid must equal rope's when rope is given.
- *   workspace  at least vidattn_fwd_window_workspace_size(...) bytes; as
- *              for vidattn_fwd it must not overlap q, k, v or o.
- * An unbounded window gives the vidattn_fwd result bit for bit. Only BF16 is
- * implemented (F32: UNSUPPORTED). */
+ * One call runs the key/value pre-pass (its key tiles in the layout's
+ * order), a planning kernel that lists per query block the key tiles its
+ * queries' windows can reach (in the workspace), and the attention over those
+ * tiles with the keys outside each query's box masked. Arguments as for
+ * vidattn_fwd, plus:
+ *   window     non-null; its grid must equal rope's when rope is given, and
+ *              its layout must be one of the VIDATTN_WINDOW_* values.
+ *   workspace  at least vidattn_fwd_window_workspace_size(..., window) bytes;
+ *              as for vidattn_fwd it must not overlap q, k, v or o.
+ * An unbounded window in the row layout gives the vidattn_fwd result bit for
+ * bit. Only BF16 is implemented (F32: UNSUPPORTED). */
 vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,
                                   int64_t heads, int64_t N, int64_t d, float softmax_scale,
                                   const vidattn_rope3d_desc* rope, const vidattn_window_desc* window,
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Workspace bytes vidattn_fwd_window needs: vidattn_fwd_workspace_size plus
- * the tile lists, 4*(ceil(N/256)*ceil(N/64)) bytes and a 256-byte-padded
- * count array. 0 for arguments vidattn_fwd_window would reject by dtype or
- * size. */
+/* Workspace bytes vidattn_fwd_window needs for this window (its layout, as
+ * resolved for VIDATTN_WINDOW_AUTO): the key/value image of nkt key tiles per
+ * (b, head), 256*d*B*heads*nkt bytes, then a 256-byte-padded count array of
+ * nqb entries and the tile lists, 4*nqb*nkt bytes. Rows: nkt = ceil(N/64),
+ * nqb = ceil(N/256) (the image is vidattn_fwd_workspace_size bytes);
+ * patches: nkt = F*ceil(H/8)*ceil(W/8), nqb = F*ceil(H/16)*ceil(W/16).
+ * 0 for arguments vidattn_fwd_window would reject by dtype, size or window. */
 size_t vidattn_fwd_window_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
-                                         int use_rope);
+                                         int use_rope, const vidattn_window_desc* window);
 
 /* Workspace bytes vidattn_fwd needs for these sizes (0 if none). Returns 0
  * also for arguments vidattn_fwd would reject; a positive size never

@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_abi_version_and_strings():
-    assert va.vidattn_abi_version() == 6 == va.ABI_VERSION
+    assert va.vidattn_abi_version() == 7 == va.ABI_VERSION
     for s, txt in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "workspace too small"),
                    (4, "HIP error")]:
         assert va.vidattn_status_string(s) == txt
@@ -235,11 +235,15 @@ def test_block_mask_words_layout():
 
 def test_window_rejects_and_sizes():
     base = va.vidattn_fwd_workspace_size(va.BF16, 2, 40, N5, 128, 1)
-    wsb = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1)
+    W = va.WindowDesc.make((21, 45, 80), (1, 4, 4), "rows")
+    wsb = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1, W)
     nqb, nkt = -(-N5 // 256), -(-N5 // 64)
     assert wsb == base + (nqb * 4 + 255) // 256 * 256 + nqb * nkt * 4
-    assert va.vidattn_fwd_window_workspace_size(va.F32, 2, 40, N5, 128, 1) == 0
-    W = va.WindowDesc.make((21, 45, 80), (1, 4, 4))
+    WP = va.WindowDesc.make((21, 45, 80), (1, 4, 4), "patches")
+    wsp = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1, WP)
+    pqb, pkt = 21 * 3 * 5, 21 * 6 * 10
+    assert wsp == 2 * 40 * 256 * 128 * pkt + (pqb * 4 + 255) // 256 * 256 + pqb * pkt * 4
+    assert va.vidattn_fwd_window_workspace_size(va.F32, 2, 40, N5, 128, 1, W) == 0
     win = lambda **kw: va.vidattn_fwd_window(**{**dict(
         q=QF, k=QF + T // 4, v=QF + T // 2, o=OF, dt=va.BF16, B=2, heads=40, N=N5, d=128, softmax_scale=0.1,
         rope=GOOD, window=W, workspace=WSF, workspace_bytes=wsb), **kw})
@@ -251,6 +255,12 @@ def test_window_rejects_and_sizes():
     assert win(workspace_bytes=wsb - 1) == 3
     assert win(workspace_bytes=base) == 3
     assert win(softmax_scale=0.0) == 1
+    assert win(window=va.WindowDesc.make((21, 45, 80), (1, 4, 4), 7)) == 1 and "layout" in va.vidattn_last_error()
+    # the patch layout needs its own (larger) image: the row layout's size is short
+    assert win(window=WP, workspace_bytes=wsp - 1) == 3
+    # a grid of 2^22 or more key patches cannot take the patch layout
+    big = va.WindowDesc.make((1 << 24, 1, 1), (0, 0, 1), "patches")
+    assert win(window=big, N=1 << 24, rope=None) == 2 and "2^22" in va.vidattn_last_error()
 
 
 def test_single_hip_runtime_whatever_the_import_order():
@@ -308,8 +318,8 @@ def test_workspace_writers_reject_q_in_the_workspace():
     assert s == 1 and "q overlaps the workspace" in va.vidattn_last_error()
     s = va.vidattn_fwd(WSF - 4096, KF, VF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD, WSF, wsb)
     assert s == 1 and "q overlaps the workspace" in va.vidattn_last_error()
-    wwsb = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1)
     W = va.WindowDesc.make((21, 45, 80), (1, 4, 4))
+    wwsb = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1, W)
     s = va.vidattn_fwd_window(WSF + wwsb - 4096, KF, VF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD, W, WSF, wwsb)
     assert s == 1 and "q overlaps the workspace" in va.vidattn_last_error()
     need = va.vidattn_fwd_block_mask_workspace_size(va.BF16, 2, 40, N5, 128, True)

@@ -59,11 +59,12 @@ def test_graph_replays_fused_attention(va):
                                              theta=wl.theta, out=o, workspace=ws), o)
 
 
-def test_graph_replays_window_attention(va):
+@pytest.mark.parametrize("layout", ["rows", "patches"])
+def test_graph_replays_window_attention(va, layout):
     wl, q, k, v = _inputs(951)
     o = torch.empty_like(q)
     B, H, N, d = q.shape
-    n = va.vidattn_fwd_window_workspace_size(0, B, H, N, d, True)
+    n = va.vidattn_fwd_window_workspace_size(0, B, H, N, d, True, va.WindowDesc.make(wl.grid, (1, 2, 3), layout))
     ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     _capture_and_replay(lambda: va.window_attention(q, k, v, (1, 2, 3), grid=wl.grid, split=wl.split,
-                                                    theta=wl.theta, out=o, workspace=ws), o)
+                                                    theta=wl.theta, layout=layout, out=o, workspace=ws), o)

@@ -416,12 +416,13 @@ def test_softmax_edge_block_sparse(va, case):
 
 @pytest.mark.parametrize("case", sorted(EDGE_CASES))
 @pytest.mark.parametrize("grid,radius", [((4, 10, 25), (1, 3, 6)), ((2, 4, 125), (1, 1, 20))])
-def test_softmax_edge_window(va, case, grid, radius):
-    _log(f"softmax edge window {case} grid={grid} radius={radius}")
+@pytest.mark.parametrize("layout", ["rows", "patches"])
+def test_softmax_edge_window(va, case, grid, radius, layout):
+    _log(f"softmax edge window {case} grid={grid} radius={radius} layout={layout}")
     qh, kh, vh = _edge_inputs(case)
     q, k, v = (parity.to_torch(x) for x in (qh, kh, vh))
     scale = 1.0 / math.sqrt(EDGE_D)
-    o = va.window_attention(q, k, v, radius, grid=grid, rope=False, scale=scale)
+    o = va.window_attention(q, k, v, radius, grid=grid, rope=False, scale=scale, layout=layout)
     torch.cuda.synchronize()
     dec = oracle.decode_bf16
     stats = _edge_compare(o, lambda h: oracle.window_attention(

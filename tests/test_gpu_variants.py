@@ -385,12 +385,19 @@ WINDOW_CASES = [
     ((1, 2, 400), 128, (44, 42, 42), 1, 1, (0, 1, 20)),
     ((1, 2, 200), 64, (16, 24, 24), 1, 2, (0, 1, 9)),
     ((3, 11, 17), 128, (0, 128, 0), 1, 2, (1, 2, 3)),
+    # patch layout: whole and ragged 16 x 16 query patches and 8 x 8 key
+    # patches, a grid smaller than one patch
+    ((2, 16, 32), 128, (44, 42, 42), 1, 2, (1, 7, 7)),
+    ((2, 24, 40), 64, (16, 24, 24), 1, 2, (0, 8, 8)),
+    ((3, 33, 18), 128, (44, 42, 42), 2, 1, (1, 9, 2)),
+    ((1, 7, 5), 128, (44, 42, 42), 1, 1, (0, 2, 2)),
 ]
 
 
-def _check_window(va, wl, host, radius, rope=True, rows=None, slices=None):
+def _check_window(va, wl, host, radius, rope=True, rows=None, slices=None, layout="auto"):
     q, k, v = (parity.to_torch(host[n]) for n in ("q", "k", "v"))
-    o = va.window_attention(q, k, v, radius, grid=wl.grid, split=wl.split, theta=wl.theta, scale=wl.scale, rope=rope)
+    o = va.window_attention(q, k, v, radius, grid=wl.grid, split=wl.split, theta=wl.theta, scale=wl.scale, rope=rope,
+                            layout=layout)
     torch.cuda.synchronize()
     parts = []
     for (b, h) in (slices or [(b, h) for b in range(wl.B) for h in range(wl.heads)]):
@@ -405,12 +412,13 @@ def _check_window(va, wl, host, radius, rope=True, rows=None, slices=None):
 @pytest.mark.parametrize("case", WINDOW_CASES,
                          ids=lambda c: f"{c[0][0]}x{c[0][1]}x{c[0][2]}-d{c[1]}-r{c[5][0]}{c[5][1]}{c[5][2]}")
 @pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
-def test_window_small(va, case, rope):
+@pytest.mark.parametrize("layout", ["rows", "patches"])
+def test_window_small(va, case, rope, layout):
     grid, d, split, B, H, radius = case
     wl = wlmod.custom(B, H, grid, d, split, seed_id=680 + d + sum(radius))
     host = parity.host_inputs(wl)
-    _log(f"window {wl.name} radius={radius} rope={rope}")
-    _, st = _check_window(va, wl, host, radius, rope)
+    _log(f"window {wl.name} radius={radius} rope={rope} layout={layout}")
+    _, st = _check_window(va, wl, host, radius, rope, layout=layout)
     _log(f"  {st}")
     assert _within(st), st
 
@@ -426,9 +434,10 @@ def test_window_unbounded_is_the_dense_attention_bitwise(va):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_window_plan_kernel_writes_the_rule(va):
-    """The planning kernel's tile lists (in the workspace tail after a call)
-    equal the rule that bench.py counts FLOPs with, on the grids of the CPU
+@pytest.mark.parametrize("layout", ["rows", "patches"])
+def test_window_plan_kernel_writes_the_rule(va, layout):
+    """The planning kernels' tile lists (in the workspace tail after a call)
+    equal the rules that bench.py counts FLOPs with, on the grids of the CPU
     rule tests."""
     import importlib.util
     import os
@@ -437,41 +446,53 @@ def test_window_plan_kernel_writes_the_rule(va):
     spec = importlib.util.spec_from_file_location("bench_module", os.path.join(root, "bench.py"))
     bench = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(bench)
-    for grid, radius in rule_tests.CASES:
+    for grid, radius in (rule_tests.PATCH_CASES if layout == "patches" else rule_tests.CASES):
         wl = wlmod.custom(1, 1, grid, 64, (16, 24, 24), seed_id=700)
         q, k, v = (parity.to_torch(wlmod.full(wl, n)) for n in ("q", "k", "v"))
-        n = va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, wl.N, wl.d, True)
+        desc = va.WindowDesc.make(grid, radius, layout)
+        n = va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, wl.N, wl.d, True, desc)
         ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
-        va.window_attention(q, k, v, radius, grid=grid, split=wl.split, workspace=ws)
+        va.window_attention(q, k, v, radius, grid=grid, split=wl.split, layout=layout, workspace=ws)
         torch.cuda.synchronize()
-        base = va.vidattn_fwd_workspace_size(va.BF16, 1, 1, wl.N, wl.d, True)
-        nqb, nkt = -(-wl.N // 256), -(-wl.N // 64)
+        F, H, W = grid
+        if layout == "rows":
+            nqb, nkt = -(-wl.N // 256), -(-wl.N // 64)
+            want = bench.window_plan_lists(wl, radius)
+        else:
+            nqb, nkt = F * -(-H // 16) * -(-W // 16), F * -(-H // 8) * -(-W // 8)
+            want = bench.window_patch_lists(wl, radius)
+        base = 256 * wl.d * nkt  # the key/value image of one (b, head)
         counts = ws[base:base + 4 * nqb].view(torch.int32).cpu().tolist()
         off = base + (4 * nqb + 255) // 256 * 256
         lists = ws[off:off + 4 * nqb * nkt].view(torch.int32).view(nqb, nkt).cpu().tolist()
         got = [row[:c] for row, c in zip(lists, counts)]
-        assert got == bench.window_plan_lists(wl, radius), (grid, radius)
+        assert got == want, (grid, radius)
 
 
-def test_window_large_wide_rows(va):
-    """The 75600-token grid (21 x 45 x 80, whole-tile test) with radius
-    (1, 7, 7); 256 sampled rows of two slices."""
+@pytest.mark.parametrize("layout", ["patches", "rows"])
+def test_window_large_wide_rows(va, layout):
+    """The 75600-token grid (21 x 45 x 80) with radius (1, 7, 7), in the
+    patch layout (the one picked for it) and in rows (whole-tile test); 256
+    sampled rows of two slices."""
     wl = wlmod.WORKLOADS[3]
     host = parity.host_inputs(wl)
     rows = wlmod.sample_rows(wl, 0, 0)
-    _log(f"window {wl.name} radius=(1, 7, 7)")
-    _, st = _check_window(va, wl, host, (1, 7, 7), rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)])
+    _log(f"window {wl.name} radius=(1, 7, 7) layout={layout}")
+    _, st = _check_window(va, wl, host, (1, 7, 7), rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)],
+                          layout=layout)
     _log(f"  {st}")
     assert _within(st), st
 
 
-def test_window_large(va):
-    """The 32760-token grid (21 x 30 x 52) with radius (2, 6, 6); 256 sampled
-    rows of two slices."""
+@pytest.mark.parametrize("layout", ["patches", "rows"])
+def test_window_large(va, layout):
+    """The 32760-token grid (21 x 30 x 52) with radius (2, 6, 6), in both
+    layouts; 256 sampled rows of two slices."""
     wl = wlmod.WORKLOADS[2]
     host = parity.host_inputs(wl)
     rows = wlmod.sample_rows(wl, 0, 0)
-    _log(f"window {wl.name} radius=(2, 6, 6)")
-    _, st = _check_window(va, wl, host, (2, 6, 6), rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)])
+    _log(f"window {wl.name} radius=(2, 6, 6) layout={layout}")
+    _, st = _check_window(va, wl, host, (2, 6, 6), rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)],
+                          layout=layout)
     _log(f"  {st}")
     assert _within(st), st

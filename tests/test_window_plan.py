@@ -1,9 +1,11 @@
-"""The planning rule of the local-window attention, on the CPU: for every
-256-query block it must list each 64-key tile that holds a key inside some
-query's box (checked by brute force over all query-key pairs on small
-grids), ascending and without repeats. The rule is the one bench.py uses to
-count FLOPs; a GPU test checks that the planning kernel writes the same
-lists."""
+"""The planning rules of the local-window attention, on the CPU. Row layout:
+for every 256-query block the list must hold each 64-key tile that holds a
+key inside some query's box (checked by brute force over all query-key pairs
+on small grids), ascending and without repeats. Patch layout: for every
+16 x 16 query patch the list must be exactly the 8 x 8 key patches that
+hold such a key. The rules are the ones bench.py uses to count FLOPs; a GPU
+test checks that the planning kernels write the same lists, and the layout
+the library picks is the one these rules say lists fewer tiles."""
 import importlib.util
 import os
 
@@ -91,3 +93,75 @@ def test_plan_on_the_benchmark_grid_is_tighter_than_whole_frames():
     wl = wlmod.WORKLOADS[5]
     counts = bench.window_plan_counts(wl, (1, 7, 7))
     assert max(counts) <= 70 and sum(counts) / len(counts) < 63
+
+
+PATCH_CASES = CASES + [
+    ((2, 16, 32), (1, 7, 7)),
+    ((2, 24, 40), (0, 8, 8)),
+    ((3, 33, 18), (1, 9, 2)),
+    ((1, 7, 5), (0, 2, 2)),      # smaller than one patch
+    ((2, 17, 17), (1, 0, 0)),
+]
+
+
+def patch_tiles_brute(grid, radius):
+    """Per query patch (frame-major), the key patches (tile index
+    (tf*ceil(H/8) + ty)*ceil(W/8) + tx) holding a key inside some query's
+    box, by brute force over all query-key pairs."""
+    F, H, W = grid
+    n = np.arange(F * H * W)
+    f, y, x = n // (H * W), (n // W) % H, n % W
+    tile = (f * -(-H // 8) + y // 8) * -(-W // 8) + x // 8
+    out = []
+    for pf in range(F):
+        for py in range(-(-H // 16)):
+            for px in range(-(-W // 16)):
+                q = n[(f == pf) & (y // 16 == py) & (x // 16 == px)]
+                vis = ((np.abs(f[q][:, None] - f[None, :]) <= radius[0])
+                       & (np.abs(y[q][:, None] - y[None, :]) <= radius[1])
+                       & (np.abs(x[q][:, None] - x[None, :]) <= radius[2]))
+                out.append(sorted(set(tile[np.nonzero(vis.any(axis=0))[0]].tolist())))
+    return out
+
+
+@pytest.mark.parametrize("grid,radius", PATCH_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_patch_plan_lists_are_exactly_the_visible_patches(grid, radius):
+    wl = wlmod.custom(1, 1, grid, 64, (16, 24, 24))
+    assert bench.window_patch_lists(wl, radius) == patch_tiles_brute(grid, radius)
+
+
+def test_library_picks_the_layout_that_lists_fewer_tiles():
+    """The window workspace size reveals the layout the library resolved
+    for VIDATTN_WINDOW_AUTO (the key/value image has ceil(N/64) tiles per
+    (b, head) in rows, F*ceil(H/8)*ceil(W/8) in patches); it must be the
+    one the restated rules say lists fewer key tiles, and a forced layout
+    must give that layout's size."""
+    import video_diffusion_transformer_rope3d_amd as va
+
+    def size(nqb, nkt, d=64):
+        return 256 * d * nkt + (4 * nqb + 255) // 256 * 256 + 4 * nqb * nkt
+
+    cases = PATCH_CASES + [((21, 45, 80), r) for r in ((1, 7, 7), (1, 3, 3), (0, 0, 80), (2, 1, 1), (21, 45, 80))]
+    picked = set()
+    for grid, radius in cases:
+        wl = wlmod.custom(1, 1, grid, 64, (16, 24, 24))
+        F, H, W = grid
+        rows = size(-(-wl.N // 256), -(-wl.N // 64))
+        patches = size(F * -(-H // 16) * -(-W // 16), F * -(-H // 8) * -(-W // 8))
+        want = bench.window_layout(wl, radius)
+        picked.add(want)
+        got = {lay: va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, wl.N, 64, True,
+                                                         va.WindowDesc.make(grid, radius, lay))
+               for lay in ("auto", "rows", "patches")}
+        assert got["rows"] == rows and got["patches"] == patches, (grid, radius)
+        assert got["auto"] == (patches if want == "patches" else rows), (grid, radius, want)
+    assert picked == {"rows", "patches"}
+
+
+def test_window_size_query_rejects_a_bad_window():
+    import video_diffusion_transformer_rope3d_amd as va
+    ok = va.WindowDesc.make((2, 3, 4), (1, 1, 1))
+    assert va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, 24, 64, True, ok) > 0
+    for bad in (None, va.WindowDesc.make((2, 3, 5), (1, 1, 1)), va.WindowDesc.make((2, 3, 4), (1, -1, 1)),
+                va.WindowDesc.make((2, 3, 4), (1, 1, 1), 3)):
+        assert va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, 24, 64, True, bad) == 0

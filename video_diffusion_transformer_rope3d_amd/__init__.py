@@ -26,7 +26,7 @@ __all__ = [
 
 BF16, F16, F32 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 SPARSE_Q_BLOCK, SPARSE_K_BLOCK = 256, 64  # VIDATTN_SPARSE_Q_BLOCK, VIDATTN_SPARSE_K_BLOCK
 NOALLOC_SCRATCH_BYTES = 64 << 20  # VIDATTN_NOALLOC_SCRATCH_BYTES
@@ -64,17 +64,22 @@ class Rope3dDesc(ctypes.Structure):
         return cls(F, H, W, d_t, d_h, d_w, float(theta))
 
 
+WINDOW_AUTO, WINDOW_ROWS, WINDOW_PATCHES = 0, 1, 2
+_WINDOW_LAYOUTS = {"auto": WINDOW_AUTO, "rows": WINDOW_ROWS, "patches": WINDOW_PATCHES}
+
+
 class WindowDesc(ctypes.Structure):
-    """vidattn_window_desc: the token grid and the window radii (frame, row,
-    column)."""
+    """vidattn_window_desc: the token grid, the window radii (frame, row,
+    column) and the tiling layout (auto, rows or patches)."""
     _fields_ = [("F", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
-                ("r_f", ctypes.c_int32), ("r_h", ctypes.c_int32), ("r_w", ctypes.c_int32)]
+                ("r_f", ctypes.c_int32), ("r_h", ctypes.c_int32), ("r_w", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, grid, radius) -> "WindowDesc":
+    def make(cls, grid, radius, layout="auto") -> "WindowDesc":
         F, H, W = (int(g) for g in grid)
         r_f, r_h, r_w = (int(r) for r in radius)
-        return cls(F, H, W, r_f, r_h, r_w)
+        return cls(F, H, W, r_f, r_h, r_w, _WINDOW_LAYOUTS[layout] if isinstance(layout, str) else int(layout))
 
 
 _LIB = None
@@ -150,7 +155,8 @@ def load() -> ctypes.CDLL:
     lib.vidattn_fwd_window.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_float,
                                        ctypes.POINTER(Rope3dDesc), ctypes.POINTER(WindowDesc), vp, sz, vp]
     lib.vidattn_fwd_window_workspace_size.restype = sz
-    lib.vidattn_fwd_window_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
+    lib.vidattn_fwd_window_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int,
+                                                      ctypes.POINTER(WindowDesc)]
     lib.vidattn_fwd_workspace_size.restype = sz
     lib.vidattn_fwd_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
     lib.vidattn_status_string.restype = ctypes.c_char_p
@@ -238,8 +244,9 @@ def vidattn_fwd_window(q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, wind
                                      workspace_bytes, stream)
 
 
-def vidattn_fwd_window_workspace_size(dt, B, heads, N, d, use_rope) -> int:
-    return load().vidattn_fwd_window_workspace_size(dt, B, heads, N, d, int(bool(use_rope)))
+def vidattn_fwd_window_workspace_size(dt, B, heads, N, d, use_rope, window) -> int:
+    return load().vidattn_fwd_window_workspace_size(dt, B, heads, N, d, int(bool(use_rope)),
+                                                    ctypes.byref(window) if window is not None else None)
 
 
 def vidattn_fwd_workspace_size(dt, B, heads, N, d, use_rope) -> int:
@@ -485,19 +492,20 @@ def attend_block_mask(q, workspace, mask, *, scale=None, grid=None, split=None, 
     return out
 
 
-def window_attention(q, k, v, radius, *, grid, split=None, theta=10000.0, scale=None, rope=True, workspace=None,
-                     out=None, stream=None):
+def window_attention(q, k, v, radius, *, grid, split=None, theta=10000.0, scale=None, rope=True, layout="auto",
+                     workspace=None, out=None, stream=None):
     """Local-window attention (BF16): each query attends to the keys within
     ``radius`` = (r_f, r_h, r_w) of its position on the token ``grid``
-    (rotary embedding on ``grid`` with ``split`` unless rope=False)."""
+    (rotary embedding on ``grid`` with ``split`` unless rope=False).
+    ``layout`` ("auto", "rows" or "patches") picks the tiling."""
     torch = _torch()
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     out = _out(out, q, stream=stream)
     rd = Rope3dDesc.make(grid, split, theta) if rope else None
-    wd = WindowDesc.make(grid, radius)
+    wd = WindowDesc.make(grid, radius, layout)
     if workspace is None:
-        n = vidattn_fwd_window_workspace_size(_dt(q), B, H, N, d, rope)
+        n = vidattn_fwd_window_workspace_size(_dt(q), B, H, N, d, rope, wd)
         workspace = _empty(n, torch.uint8, q.device, stream) if n else None
     ptr, nbytes = _ws(workspace, q)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)

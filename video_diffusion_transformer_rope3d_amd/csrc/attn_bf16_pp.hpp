@@ -65,12 +65,25 @@ namespace vidattn {
 // mode 2 (W >= 64): a 64-key tile spans at most two grid rows and is tested
 // as a whole; mode 1 (W >= 8): each run of 8 keys spans at most two rows;
 // mode 0: any grid, integer division and per-key stepping.
+// mode 3 (patch layout): key tile t is the 8 x 8 patch (tf, ty, tx),
+// t = (tf*tyn + ty)*txn + tx, with key 8r + c at grid row 8ty + r, column
+// 8tx + c (keys past the grid's edge are zero in the workspace and never
+// visible), and query block b the 16 x 16 patch (f, py, px) of one frame,
+// b = (f*pyn + py)*pxn + px, with row 16i + j of the block at grid row
+// 16py + i, column 16px + j (rows past the edge compute nothing that is
+// stored). The host sets it only when tile and block indices are below 2^22
+// (their decode uses the same fp32 reciprocal split).
 struct WindowParams {
   int F, H, W;
   int rf, rh, rw;
   int mode;
   float invW, invH;
+  int tyn, txn, pyn, pxn;
+  float invtxn, invtyn, invpxn, invpyn;
 };
+
+// (int)fma(k, inv, inv / 2) = k / n for 0 <= k < 2^22 and inv = 1/n in fp32.
+__device__ __forceinline__ int div_small(int k, float inv) { return (int)__builtin_fmaf((float)k, inv, 0.5f * inv); }
 
 template <int D, int NS, bool SPARSE, bool WIN = false>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
@@ -136,10 +149,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       return j;
     }
   };
+  // This lane's query row: its row index in Q and O, and whether it exists
+  // (in the patch layout, rows past the grid's edge do not).
+  int qtok;
+  bool qvalid;
+  {
+    const int r = wave * 32 + qi;
+    if (WIN && wp.mode == 3) {
+      const int b2 = div_small(qt, wp.invpxn), px = qt - b2 * wp.pxn;
+      const int f = div_small(b2, wp.invpyn), py = b2 - f * wp.pyn;
+      const int y = 16 * py + (r >> 4), x = 16 * px + (r & 15);
+      qvalid = y < wp.H && x < wp.W;
+      qtok = qvalid ? (f * wp.H + y) * wp.W + x : 0;
+    } else {
+      qtok = qt * BR + r;
+      qvalid = qtok < Nq;
+      if (!qvalid) qtok = 0;
+    }
+  }
   if (SPARSE && nt == 0) {  // no key visited: O = 0 for the block's rows
-    const int q = qt * BR + wave * 32 + qi;
-    if (q < Nq) {
-      uint16_t* orow = O + ((int64_t)bh * Nq + q) * D;
+    if (qvalid) {
+      uint16_t* orow = O + ((int64_t)bh * Nq + qtok) * D;
 #pragma unroll
       for (int c = 0; c < D / 8; c += 2)
         *reinterpret_cast<u32x4*>(orow + 8 * (c + g)) = u32x4{0u, 0u, 0u, 0u};
@@ -170,13 +200,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // Their loads are issued before any tile load, so waiting for tile 0 covers them.
   half8 qreg[KSTEPS];
   {
-    const int q = qt * BR + wave * 32 + qi;
-    const uint16_t* qrow = Q + ((int64_t)bh * Nq + (q < Nq ? q : 0)) * D;
+    const uint16_t* qrow = Q + ((int64_t)bh * Nq + qtok) * D;
     u32x4 raw[KSTEPS];
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * g);
     // rotary position of this row: its token index in the grid
-    int pos = q < Nq ? q : 0;
+    int pos = qtok;
     if (qidx) {
       const int t = qidx[pos];
       pos = t < 0 ? 0 : (t < N ? t : N - 1);
@@ -250,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qreg[s][j] = (_Float16)(q < Nq ? x[j] * qscale : 0.f);
+      for (int j = 0; j < 8; ++j) qreg[s][j] = (_Float16)(qvalid ? x[j] * qscale : 0.f);
     }
   }
 
@@ -267,8 +296,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // row wrap, [wlo, wend) counted from the run's start as W - c0 + column.
   int flo = 0, ylo = 0, clo = 0, cend = 0, wlo = 0, wend = 0;
   if constexpr (WIN) {
-    const int qrow = qt * BR + wave * 32 + qi;
-    const int t = qrow < N ? qrow : N - 1;
+    const int t = qtok;
     const int hw = wp.H * wp.W;
     const int qf = t / hw;
     const int qy = (t - qf * hw) / wp.W;
@@ -369,7 +397,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   constexpr int kWaitNewer = STAGE_LOADS * (NS - 2);
   constexpr int kVmcntNewer = (kWaitNewer & 0xF) | ((kWaitNewer >> 4) << 14) | (0x7 << 4) | (0xF << 8);
   constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
-  const int tail = N - (nkt - 1) * KT;  // valid keys of the last key tile, 1..KT
+  // valid keys of the last key tile, 1..KT (the patch layout's edge keys are
+  // masked by the window test instead)
+  const int tail = WIN && wp.mode == 3 ? KT : N - (nkt - 1) * KT;
 
   // Barrier that opens tile period i: tile i must have landed (a loader's
   // loads of the newer tiles may stay in flight).
@@ -392,7 +422,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       const int base = tile * KT;
       const unsigned fspan = 2u * wp.rf, yspan = 2u * wp.rh, xspan = 2u * wp.rw;
       const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
-      if (wp.mode == 2) {
+      if (wp.mode == 3) {
+        // patch tile (tf, ty, tx): run u of this lane is patch row 2u + g,
+        // all 8 columns; the columns it sees are the same for every row
+        const int t2 = div_small(tile, wp.invtxn), tx = tile - t2 * wp.txn;
+        const int tf = div_small(t2, wp.invtyn), ty = t2 - tf * wp.tyn;
+        const int x0 = 8 * tx;
+        const int a = clo - x0 < 0 ? 0 : (clo - x0 > 8 ? 8 : clo - x0);
+        const int b = cend - x0 < a ? a : (cend - x0 > 8 ? 8 : cend - x0);
+        const unsigned cm = (1u << b) - (1u << a);
+        const bool fok = (unsigned)(tf - flo) <= fspan;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int y = 8 * ty + 2 * u + g;
+          const bool rok = fok & ((unsigned)(y - ylo) <= yspan) & (y < wp.H);
+          vis |= (rok ? cm : 0u) << (8 * u);
+        }
+      } else if (wp.mode == 2) {
         // the tile [base, base + 64) lies in rows rb and rb + 1; the visible
         // keys of each row form one range of tile offsets
         auto bits64 = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..63
@@ -718,10 +764,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
 
   // ---- epilogue: O = O^T / l, rounded to bf16.
   // Output register i of lane (q, g) in head-dim block db is d = 32db + 8(i/4) + 4g + i%4.
-  const int q = qt * BR + wave * 32 + qi;
   const float inv = 1.0f / xor32_sum(l);
-  if (q < Nq) {
-    uint16_t* orow = O + ((int64_t)bh * Nq + q) * D;
+  if (qvalid) {
+    uint16_t* orow = O + ((int64_t)bh * Nq + qtok) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll

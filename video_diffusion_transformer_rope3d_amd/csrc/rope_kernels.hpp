@@ -106,11 +106,34 @@ __global__ __launch_bounds__(256) void rope3d_kernel(const TIn* in, TOut* out, i
 //   V part: 1 KB blocks, block (db, m) for head-dim block db < D/32 and key
 //           step m < 4 (16 keys); lane l = i + 32g holds V[16m + 8g + j][32db + i],
 //           j < 8 (bf16): the A operand of the V^T.P^T product.
-// Keys past N are zero in both parts.
+// Key slots that hold no token (past N, or outside the grid) are zero in
+// both parts.
+//
+// Which tokens a tile holds: tile t holds tokens 64t .. 64t+63 (row order),
+// or, in the patch order of the local-window attention, the 8 x 8 patch
+// (tf, ty, tx) of the grid, t = (tf*tyn + ty)*txn + tx, whose key 8r + c is
+// the token at frame tf, row 8ty + r, column 8tx + c.
+struct TileMap {
+  int patch;  // 0: row order, 1: patch order
+  int H, W, tyn, txn;
+
+  // token of key kk < 64 of tile t, -1 for an empty slot
+  __device__ __forceinline__ int token(int t, int kk, int N) const {
+    if (!patch) {
+      const int n = t * 64 + kk;
+      return n < N ? n : -1;
+    }
+    const int tf = t / (tyn * txn), rest = t - tf * (tyn * txn);
+    const int ty = rest / txn, tx = rest - ty * txn;
+    const int y = 8 * ty + (kk >> 3), x = 8 * tx + (kk & 7);
+    return y < H && x < W ? (tf * H + y) * W + x : -1;
+  }
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                       uint8_t* __restrict__ ws, int N, int nkt, int64_t nbh,
-                                                      int bh_per_block, RopeParams rp) {
+                                                      int bh_per_block, RopeParams rp, TileMap map) {
   constexpr int KT = 64;
   constexpr int KSTEPS = D / 16;
   constexpr int TILE = KT * D * 2;
@@ -120,7 +143,6 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
 
   const int t = threadIdx.x;
   const int tile = blockIdx.x;
-  const int n0 = tile * KT;
 
   int ksrc[SLOTS];  // source key of the slot (-1: past N)
   int kchunk[SLOTS];
@@ -131,16 +153,21 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
     const int blk = slot >> 6, lane = slot & 63;
     const int i = lane & 31, g = lane >> 5;
     const int kb = blk / KSTEPS, s = blk - kb * KSTEPS;
-    const int n = n0 + 32 * kb + rho32(i);
-    ksrc[r] = n < N ? n : -1;
+    const int n = map.token(tile, 32 * kb + rho32(i), N);
+    ksrc[r] = n;
     kchunk[r] = 2 * s + g;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       cs[r][j] = 1.f;
       sn[r][j] = 0.f;
-      if (rp.enabled && n < N) rope_cos_sin(rp, n, 4 * kchunk[r] + j, cs[r][j], sn[r][j]);
+      if (rp.enabled && n >= 0) rope_cos_sin(rp, n, 4 * kchunk[r] + j, cs[r][j], sn[r][j]);
     }
   }
+
+  // token of the value row each thread stages (SLOTS rows of D/8 chunks)
+  int vsrc[SLOTS];
+#pragma unroll
+  for (int r = 0; r < SLOTS; ++r) vsrc[r] = map.token(tile, (t + 256 * r) / (D / 8), N);
 
   const int64_t bh0 = (int64_t)blockIdx.y * bh_per_block;
   const int64_t bh1 = bh0 + bh_per_block < nbh ? bh0 + bh_per_block : nbh;
@@ -174,7 +201,7 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
       const int ch = t + 256 * r;
       const int row = ch / (D / 8), col8 = ch - row * (D / 8);
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (n0 + row < N) w = *reinterpret_cast<const u32x4*>(Vbh + (int64_t)(n0 + row) * D + 8 * col8);
+      if (vsrc[r] >= 0) w = *reinterpret_cast<const u32x4*>(Vbh + (int64_t)vsrc[r] * D + 8 * col8);
       *reinterpret_cast<u32x4*>(vs + row * VPAD + 8 * col8) = w;
     }
     __syncthreads();

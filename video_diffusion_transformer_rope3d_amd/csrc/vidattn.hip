@@ -324,19 +324,22 @@ vidattn_status validate_fwd(Phase ph, const void* q, const void* k, const void* 
 }
 
 // Launch the key/value pre-pass (arguments already validated).
+// map: the token order of the bf16 key tiles (row order unless given), with
+// nkt tiles per (b, head).
 vidattn_status launch_prepare(const void* k, const void* v, vidattn_dtype dt, int64_t nbh, int64_t N, int64_t d,
-                              const RopeParams& rp, void* workspace, hipStream_t st) {
+                              const RopeParams& rp, void* workspace, hipStream_t st,
+                              const TileMap& map = TileMap{0, 1, 1, 1, 1}, int64_t nkt_map = 0) {
   if (dt == VIDATTN_BF16) {
-    const int nkt = (int)((N + kKT - 1) / kKT);
+    const int nkt = map.patch ? (int)nkt_map : (int)((N + kKT - 1) / kKT);
     const int grp = bh_group(nkt, nbh);
     const dim3 pgrid((unsigned)nkt, (unsigned)((nbh + grp - 1) / grp));
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (d == 128)
       hipLaunchKernelGGL((prep_kv_kernel<128>), pgrid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
-                         static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp);
+                         static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp, map);
     else
       hipLaunchKernelGGL((prep_kv_kernel<64>), pgrid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
-                         static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp);
+                         static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp, map);
     return hip_check("bf16 key/value pre-pass launch");
   }
   if (!rp.enabled) return VIDATTN_OK;
@@ -359,7 +362,8 @@ struct AttendExtras {
   int maxb = 0;
   int lists_shared = 0;  // one list per query block for every (b, head)
   bool window = false;   // mask keys outside each query's box
-  WindowParams wp{1, 1, 1, 0, 0, 0, 0, 1.f, 1.f};
+  WindowParams wp{1, 1, 1, 0, 0, 0, 0, 1.f, 1.f, 1, 1, 1, 1, 1.f, 1.f, 1.f, 1.f};
+  int64_t nkt = 0, ntq = 0;  // > 0: key tiles and query blocks of the patch layout
 };
 
 template <int D, bool SPARSE, bool WIN>
@@ -377,8 +381,8 @@ vidattn_status launch_attend(const void* q, const void* k, const void* v, const 
   const float qscale = softmax_scale * log2e;
   if (dt == VIDATTN_BF16) {
     const int64_t Nq = x.Nq < 0 ? N : x.Nq;
-    const int nkt = (int)((N + kKT - 1) / kKT);
-    const int ntq = (int)((Nq + kBR - 1) / kBR);
+    const int nkt = x.nkt > 0 ? (int)x.nkt : (int)((N + kKT - 1) / kKT);
+    const int ntq = x.ntq > 0 ? (int)x.ntq : (int)((Nq + kBR - 1) / kBR);
     const int total = (int)(nbh * ntq);
     const uint8_t* ws = static_cast<const uint8_t*>(workspace);
     const bool sparse = x.kvb != nullptr;
@@ -508,10 +512,6 @@ vidattn_status vidattn_fwd_attend_block_sparse(const void* q, const void* worksp
   return ok();
 }
 
-
-// Workspace of the local-window attention: the key/value image, then the
-// per-query-block tile counts (padded to 256 bytes), then the tile lists
-// (ceil(N/256) rows of ceil(N/64) entries).
 // Tile lists built from a block bit mask, in the workspace tail after the
 // prepared key/value image: counts [B*heads*nqb] (256-byte padded), then
 // lists [B*heads*nqb][nkt].
@@ -520,12 +520,47 @@ static size_t block_mask_list_bytes(int64_t nbh, int64_t N) {
   return (size_t)((nbh * nqb * 4 + 255) / 256 * 256 + nbh * nqb * nkt * 4);
 }
 
-static size_t window_plan_bytes(int64_t N) {
-  const int64_t nqb = (N + kBR - 1) / kBR, nkt = (N + kKT - 1) / kKT;
-  return (size_t)((nqb * 4 + 255) / 256 * 256 + nqb * nkt * 4);
+// Layout of one local-window call and its tile counts (see
+// vidattn_window_desc and window_plan.hpp). Its workspace: the key/value
+// image of nkt tiles per (b, head), then the per-query-block tile counts
+// (padded to 256 bytes), then the tile lists (nqb rows of nkt entries).
+struct WindowGeom {
+  int layout = VIDATTN_WINDOW_ROWS;
+  int64_t nkt = 0, nqb = 0;          // key tiles per (b, head), query blocks
+  int tyn = 1, txn = 1, pyn = 1, pxn = 1;  // patch counts per axis (patch layout)
+  int rf = 0, rh = 0, rw = 0;        // radii clipped to the grid
+};
+
+// Key tiles the row layout lists in all (host count of window_plan_kernel).
+static int64_t rows_tiles_listed(int64_t N, int F, int H, int W, int rf, int rh) {
+  const int nqb = (int)((N + kBR - 1) / kBR);
+  int64_t total = 0;
+  for (int i = 0; i < nqb; ++i)
+    window_rows_plan(i, (int)N, F, H, W, rf, rh, [&](int t0, int t1) { total += t1 - t0 + 1; });
+  return total;
 }
 
-static vidattn_status check_window(const vidattn_window_desc* w, int64_t N, const vidattn_rope3d_desc* rope) {
+// Key tiles the patch layout lists in all: the count of patch (f, py, px) is
+// the product of its frame, row and column spans, so the sum factors.
+static int64_t patch_tiles_listed(const WindowGeom& g, int F, int H, int W) {
+  int64_t sf = 0, sy = 0, sx = 0;
+  for (int f = 0; f < F; ++f) sf += std::min(F - 1, f + g.rf) - std::max(0, f - g.rf) + 1;
+  for (int p = 0; p < g.pyn; ++p) {
+    int lo, hi;
+    window_patch_span(p, H, g.rh, lo, hi);
+    sy += hi - lo + 1;
+  }
+  for (int p = 0; p < g.pxn; ++p) {
+    int lo, hi;
+    window_patch_span(p, W, g.rw, lo, hi);
+    sx += hi - lo + 1;
+  }
+  return sf * sy * sx;
+}
+
+// Checks the window against N and rope and resolves its layout.
+static vidattn_status window_geom(const vidattn_window_desc* w, int64_t N, const vidattn_rope3d_desc* rope,
+                                  WindowGeom* g) {
   if (!w) return fail(VIDATTN_ERR_INVALID_ARG, "window must be non-null");
   if (w->F < 1 || w->H < 1 || w->W < 1) return fail(VIDATTN_ERR_INVALID_ARG, "window grid extents must be >= 1");
   int64_t hw, fhw;
@@ -534,14 +569,58 @@ static vidattn_status check_window(const vidattn_window_desc* w, int64_t N, cons
   if (w->r_f < 0 || w->r_h < 0 || w->r_w < 0) return fail(VIDATTN_ERR_INVALID_ARG, "window radii must be >= 0");
   if (rope && (rope->F != w->F || rope->H != w->H || rope->W != w->W))
     return fail(VIDATTN_ERR_INVALID_ARG, "window and rotary grids differ");
+  if (w->layout != VIDATTN_WINDOW_AUTO && w->layout != VIDATTN_WINDOW_ROWS && w->layout != VIDATTN_WINDOW_PATCHES)
+    return fail(VIDATTN_ERR_INVALID_ARG, "window layout %d is not a VIDATTN_WINDOW_* value", (int)w->layout);
+  // N <= kMaxN (checked by the caller) bounds every extent and count below
+  const int F = (int)w->F, H = (int)w->H, W = (int)w->W;
+  // a radius at or beyond the grid extent reaches the whole axis
+  g->rf = (int)std::min<int64_t>(w->r_f, F);
+  g->rh = (int)std::min<int64_t>(w->r_h, H);
+  g->rw = (int)std::min<int64_t>(w->r_w, W);
+  g->layout = VIDATTN_WINDOW_ROWS;
+  g->nkt = (N + kKT - 1) / kKT;
+  g->nqb = (N + kBR - 1) / kBR;
+  const int tyn = (H + 7) / 8, txn = (W + 7) / 8, pyn = (H + 15) / 16, pxn = (W + 15) / 16;
+  const int64_t pnkt = (int64_t)F * tyn * txn, pnqb = (int64_t)F * pyn * pxn;
+  // the kernel decodes patch indices with an fp32 reciprocal split
+  const bool patch_ok = pnkt < (int64_t(1) << 22) && pnqb < (int64_t(1) << 22);
+  if (w->layout == VIDATTN_WINDOW_PATCHES && !patch_ok)
+    return fail(VIDATTN_ERR_UNSUPPORTED, "patch layout needs fewer than 2^22 key and query patches");
+  if (w->layout == VIDATTN_WINDOW_ROWS || !patch_ok) return VIDATTN_OK;
+  WindowGeom p = *g;
+  p.layout = VIDATTN_WINDOW_PATCHES;
+  p.nkt = pnkt;
+  p.nqb = pnqb;
+  p.tyn = tyn;
+  p.txn = txn;
+  p.pyn = pyn;
+  p.pxn = pxn;
+  // every listed tile costs the same (256 queries x 64 keys) in both layouts
+  if (w->layout == VIDATTN_WINDOW_PATCHES ||
+      patch_tiles_listed(p, F, H, W) < rows_tiles_listed(N, F, H, W, g->rf, g->rh))
+    *g = p;
   return VIDATTN_OK;
 }
 
+// bf16 key/value image and tile lists of a window call.
+static size_t window_image_bytes(int64_t nbh, int64_t d, const WindowGeom& g) {
+  return (size_t)(4 * nbh * g.nkt * kKT * d);
+}
+static size_t window_plan_bytes(const WindowGeom& g) {
+  return (size_t)((g.nqb * 4 + 255) / 256 * 256 + g.nqb * g.nkt * 4);
+}
+
 size_t vidattn_fwd_window_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
-                                         int use_rope) {
+                                         int use_rope, const vidattn_window_desc* window) {
   if (dt != VIDATTN_BF16) return 0;
   const size_t base = vidattn_fwd_workspace_size(dt, B, heads, N, d, use_rope);
-  return base ? base + window_plan_bytes(N) : 0;
+  if (!base) return 0;
+  WindowGeom g;
+  const std::string saved = g_last_error;  // a size query leaves the last error alone
+  const vidattn_status s = window_geom(window, N, nullptr, &g);
+  g_last_error = saved;
+  if (s != VIDATTN_OK) return 0;
+  return window_image_bytes(B * heads, d, g) + window_plan_bytes(g);
 }
 
 vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, void* o, vidattn_dtype dt, int64_t B,
@@ -551,40 +630,61 @@ vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, v
   if (dt != VIDATTN_BF16)
     return fail(dt == VIDATTN_F32 || dt == VIDATTN_F16 ? VIDATTN_ERR_UNSUPPORTED : VIDATTN_ERR_INVALID_ARG,
                 "local-window attention is implemented for BF16");
-  if (N >= 1 && N <= kMaxN)
-    if (vidattn_status s = check_window(window, N, rope)) return s;
-  const size_t plan = N >= 1 && N <= kMaxN ? window_plan_bytes(N) : 0;
+  WindowGeom g;
+  size_t extra = 0;  // workspace beyond vidattn_fwd_workspace_size
+  const bool sizes_ok = N >= 1 && N <= kMaxN && B >= 1 && heads >= 1 && B <= kMaxBH && heads <= kMaxBH &&
+                        B * heads <= kMaxBH && (d == 64 || d == 128);
+  if (N >= 1 && N <= kMaxN) {
+    if (vidattn_status s = window_geom(window, N, rope, &g)) return s;
+    if (sizes_ok)
+      extra = window_image_bytes(B * heads, d, g) + window_plan_bytes(g) -
+              vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
+  }
   if (vidattn_status s = validate_fwd(Phase::kFused, q, k, v, o, dt, B, heads, N, d, softmax_scale, rope, workspace,
-                                      workspace_bytes, -1, plan))
+                                      workspace_bytes, -1, extra))
     return s;
   if (!window) return fail(VIDATTN_ERR_INVALID_ARG, "window must be non-null");
+  const int64_t nbh = B * heads;
+  if (nbh * g.nqb > (int64_t)INT32_MAX / (kNW * 64))
+    return fail(VIDATTN_ERR_UNSUPPORTED, "problem too large for one launch");
   const RopeParams rp = make_rope(rope);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  if (vidattn_status s = launch_prepare(k, v, dt, B * heads, N, d, rp, workspace, st)) return s;
-  const int64_t nqb = (N + kBR - 1) / kBR, nkt = (N + kKT - 1) / kKT;
-  uint8_t* tail = static_cast<uint8_t*>(workspace) + vidattn_fwd_workspace_size(dt, B, heads, N, d, rope != nullptr);
+  const bool patch = g.layout == VIDATTN_WINDOW_PATCHES;
+  const int F = (int)window->F, H = (int)window->H, W = (int)window->W;
+  const TileMap map{patch ? 1 : 0, H, W, g.tyn, g.txn};
+  if (vidattn_status s = launch_prepare(k, v, dt, nbh, N, d, rp, workspace, st, map, g.nkt)) return s;
+  uint8_t* tail = static_cast<uint8_t*>(workspace) + window_image_bytes(nbh, d, g);
   int32_t* kvc = reinterpret_cast<int32_t*>(tail);
-  int32_t* kvb = reinterpret_cast<int32_t*>(tail + (nqb * 4 + 255) / 256 * 256);
-  hipLaunchKernelGGL(window_plan_kernel, dim3((unsigned)((nqb + 255) / 256)), dim3(256), 0, st, kvb, kvc, (int)N,
-                     (int)nqb, (int)nkt, (int)window->F, (int)window->H, (int)window->W,
-                     (int)std::min<int64_t>(window->r_f, window->F), (int)std::min<int64_t>(window->r_h, window->H));
+  int32_t* kvb = reinterpret_cast<int32_t*>(tail + (g.nqb * 4 + 255) / 256 * 256);
+  const dim3 pgrid((unsigned)((g.nqb + 255) / 256));
+  if (patch)
+    hipLaunchKernelGGL(window_plan_patch_kernel, pgrid, dim3(256), 0, st, kvb, kvc, (int)g.nqb, (int)g.nkt, F, H, W,
+                       g.rf, g.rh, g.rw, g.tyn, g.txn, g.pyn, g.pxn);
+  else
+    hipLaunchKernelGGL(window_plan_kernel, pgrid, dim3(256), 0, st, kvb, kvc, (int)N, (int)g.nqb, (int)g.nkt, F, H,
+                       W, g.rf, g.rh);
   if (vidattn_status s = hip_check("window plan launch")) return s;
   AttendExtras x;
   x.kvb = kvb;
   x.kvc = kvc;
-  x.maxb = (int)nkt;
+  x.maxb = (int)g.nkt;
   x.lists_shared = 1;
   x.window = true;
-  // a radius at or beyond the grid extent reaches the whole axis
-  const int rf = (int)std::min<int64_t>(window->r_f, window->F), rh = (int)std::min<int64_t>(window->r_h, window->H),
-            rw = (int)std::min<int64_t>(window->r_w, window->W);
-  // key decode (see WindowParams): the fp32 split needs key indices (up to
-  // nkt * 64 - 1) below 2^22; rows of >= 64 tokens allow the whole-tile test
-  const bool small_n = nkt * kKT < (int64_t(1) << 22);
-  const int mode = !small_n ? 0 : (window->W >= 64 ? 2 : (window->W >= 8 ? 1 : 0));
-  x.wp = WindowParams{(int)window->F, (int)window->H, (int)window->W, rf, rh, rw, mode,
-                      (float)(1.0 / (double)window->W), (float)(1.0 / (double)window->H)};
-  if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, B * heads, N, d, softmax_scale, rp, st, x)) return s;
+  int mode;
+  if (patch) {
+    mode = 3;
+    x.nkt = g.nkt;
+    x.ntq = g.nqb;
+  } else {
+    // key decode (see WindowParams): the fp32 split needs key indices (up to
+    // nkt * 64 - 1) below 2^22; rows of >= 64 tokens allow the whole-tile test
+    const bool small_n = g.nkt * kKT < (int64_t(1) << 22);
+    mode = !small_n ? 0 : (W >= 64 ? 2 : (W >= 8 ? 1 : 0));
+  }
+  auto inv = [](int n) { return (float)(1.0 / (double)n); };
+  x.wp = WindowParams{F, H, W, g.rf, g.rh, g.rw, mode, inv(W), inv(H), g.tyn, g.txn, g.pyn, g.pxn,
+                      inv(g.txn), inv(g.tyn), inv(g.pxn), inv(g.pyn)};
+  if (vidattn_status s = launch_attend(q, k, v, workspace, o, dt, nbh, N, d, softmax_scale, rp, st, x)) return s;
   return ok();
 }
 
