@@ -114,12 +114,13 @@ __global__ __launch_bounds__(256) void rope3d_kernel(const TIn* in, TOut* out, i
 // (tf, ty, tx) of the grid, t = (tf*tyn + ty)*txn + tx, whose key 8r + c is
 // the token at frame tf, row 8ty + r, column 8tx + c.
 struct TileMap {
-  int patch;  // 0: row order, 1: patch order
+  int patch;  // 0: row order, 1: patch order (the kernel's PATCH)
   int H, W, tyn, txn;
 
   // token of key kk < 64 of tile t, -1 for an empty slot
+  template <bool PATCH>
   __device__ __forceinline__ int token(int t, int kk, int N) const {
-    if (!patch) {
+    if (!PATCH) {
       const int n = t * 64 + kk;
       return n < N ? n : -1;
     }
@@ -130,7 +131,7 @@ struct TileMap {
   }
 };
 
-template <int D>
+template <int D, bool PATCH = false>
 __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                       uint8_t* __restrict__ ws, int N, int nkt, int64_t nbh,
                                                       int bh_per_block, RopeParams rp, TileMap map) {
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
     const int blk = slot >> 6, lane = slot & 63;
     const int i = lane & 31, g = lane >> 5;
     const int kb = blk / KSTEPS, s = blk - kb * KSTEPS;
-    const int n = map.token(tile, 32 * kb + rho32(i), N);
+    const int n = map.token<PATCH>(tile, 32 * kb + rho32(i), N);
     ksrc[r] = n;
     kchunk[r] = 2 * s + g;
 #pragma unroll
@@ -163,11 +164,6 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
       if (rp.enabled && n >= 0) rope_cos_sin(rp, n, 4 * kchunk[r] + j, cs[r][j], sn[r][j]);
     }
   }
-
-  // token of the value row each thread stages (SLOTS rows of D/8 chunks)
-  int vsrc[SLOTS];
-#pragma unroll
-  for (int r = 0; r < SLOTS; ++r) vsrc[r] = map.token(tile, (t + 256 * r) / (D / 8), N);
 
   const int64_t bh0 = (int64_t)blockIdx.y * bh_per_block;
   const int64_t bh1 = bh0 + bh_per_block < nbh ? bh0 + bh_per_block : nbh;
@@ -201,7 +197,8 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
       const int ch = t + 256 * r;
       const int row = ch / (D / 8), col8 = ch - row * (D / 8);
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (vsrc[r] >= 0) w = *reinterpret_cast<const u32x4*>(Vbh + (int64_t)vsrc[r] * D + 8 * col8);
+      const int n = map.token<PATCH>(tile, row, N);
+      if (n >= 0) w = *reinterpret_cast<const u32x4*>(Vbh + (int64_t)n * D + 8 * col8);
       *reinterpret_cast<u32x4*>(vs + row * VPAD + 8 * col8) = w;
     }
     __syncthreads();

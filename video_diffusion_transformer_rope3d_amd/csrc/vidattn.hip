@@ -334,12 +334,15 @@ vidattn_status launch_prepare(const void* k, const void* v, vidattn_dtype dt, in
     const int grp = bh_group(nkt, nbh);
     const dim3 pgrid((unsigned)nkt, (unsigned)((nbh + grp - 1) / grp));
     uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    const uint16_t* vv = static_cast<const uint16_t*>(v);
+    auto launch = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, pgrid, dim3(256), 0, st, kk, vv, ws, (int)N, nkt, nbh, grp, rp, map);
+    };
     if (d == 128)
-      hipLaunchKernelGGL((prep_kv_kernel<128>), pgrid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
-                         static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp, map);
+      launch(map.patch ? prep_kv_kernel<128, true> : prep_kv_kernel<128, false>);
     else
-      hipLaunchKernelGGL((prep_kv_kernel<64>), pgrid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
-                         static_cast<const uint16_t*>(v), ws, (int)N, nkt, nbh, grp, rp, map);
+      launch(map.patch ? prep_kv_kernel<64, true> : prep_kv_kernel<64, false>);
     return hip_check("bf16 key/value pre-pass launch");
   }
   if (!rp.enabled) return VIDATTN_OK;
