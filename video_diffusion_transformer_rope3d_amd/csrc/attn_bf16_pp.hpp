@@ -41,9 +41,10 @@
 // (b, head, 256-query block) visits only the 64-key tiles listed in
 // kvb[.][0 .. kvc[.]-1] (ascending), so "tile j" of the loop is the j-th
 // listed tile; a block with no listed tile gets O = 0; the lists may be
-// shared by every (b, head) (lists_shared). Local window (WIN, on top of
-// SPARSE): in the listed tiles, keys outside the box of radii (r_f, r_h,
-// r_w) around the query's grid position get -inf. Indices read from device
+// shared by every (b, head) (lists_shared). Local window (WIN != kWinNone,
+// on top of SPARSE): in the listed tiles, keys outside the box of radii
+// (r_f, r_h, r_w) around the query's grid position get -inf (row layout) or
+// a score below -3e38 (patch layout), which exp2 takes to 0 all the same. Indices read from device
 // memory are clamped into range, so no input can address outside the
 // workspace. A row's m is unset until its first tile with a visible key
 // (in the dense case: the first tile); the exact step runs on that tile, so
@@ -65,14 +66,15 @@ namespace vidattn {
 // mode 2 (W >= 64): a 64-key tile spans at most two grid rows and is tested
 // as a whole; mode 1 (W >= 8): each run of 8 keys spans at most two rows;
 // mode 0: any grid, integer division and per-key stepping.
-// mode 3 (patch layout): key tile t is the 8 x 8 patch (tf, ty, tx),
-// t = (tf*tyn + ty)*txn + tx, with key 8r + c at grid row 8ty + r, column
-// 8tx + c (keys past the grid's edge are zero in the workspace and never
-// visible), and query block b the 16 x 16 patch (f, py, px) of one frame,
-// b = (f*pyn + py)*pxn + px, with row 16i + j of the block at grid row
-// 16py + i, column 16px + j (rows past the edge compute nothing that is
-// stored). The host sets it only when tile and block indices are below 2^22
-// (their decode uses the same fp32 reciprocal split).
+// The patch layout (WIN == kWinPatch) does not use mode: key tile t is the
+// 8 x 8 patch (tf, ty, tx), t = (tf*tyn + ty)*txn + tx, with key 8r + c at
+// grid row 8ty + r, column 8tx + c (keys past the grid's edge are zero in
+// the workspace and never visible), and query block b the 16 x 16 patch
+// (f, py, px) of one frame, b = (f*pyn + py)*pxn + px, with row 16i + j of
+// the block at grid row 16py + i, column 16px + j (rows past the edge
+// compute nothing that is stored). The host uses it only when tile and block
+// indices are below 2^22 (their decode uses the fp32 reciprocal split).
+constexpr int kWinNone = 0, kWinRows = 1, kWinPatch = 2;
 struct WindowParams {
   int F, H, W;
   int rf, rh, rw;
@@ -85,13 +87,13 @@ struct WindowParams {
 // (int)fma(k, inv, inv / 2) = k / n for 0 <= k < 2^22 and inv = 1/n in fp32.
 __device__ __forceinline__ int div_small(int k, float inv) { return (int)__builtin_fmaf((float)k, inv, 0.5f * inv); }
 
-template <int D, int NS, bool SPARSE, bool WIN = false>
+template <int D, int NS, bool SPARSE, int WIN = kWinNone>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ ws, uint16_t* __restrict__ O, int N, int nkt, int Nq,
     int ntq, int total_wg, float qscale, RopeParams rp, const int32_t* __restrict__ qidx,
     const int32_t* __restrict__ kvb, const int32_t* __restrict__ kvc, int maxb, int lists_shared,
     WindowParams wp) {
-  static_assert(SPARSE || !WIN, "the window visits listed tiles");
+  static_assert(SPARSE || WIN == kWinNone, "the window visits listed tiles");
   constexpr int NW = 8;
   constexpr int KT = 64;
   constexpr int BR = NW * 32;
@@ -150,17 +152,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     }
   };
   // This lane's query row: its row index in Q and O, and whether it exists
-  // (in the patch layout, rows past the grid's edge do not).
+  // (in the patch layout, rows past the grid's edge do not; their grid
+  // position (pf, py0 + r/16, px0 + r%16) still serves the rotation).
   int qtok;
   bool qvalid;
+  int pf = 0, py0 = 0, px0 = 0;  // the patch's frame, first row and first column
   {
     const int r = wave * 32 + qi;
-    if (WIN && wp.mode == 3) {
+    if constexpr (WIN == kWinPatch) {
       const int b2 = div_small(qt, wp.invpxn), px = qt - b2 * wp.pxn;
-      const int f = div_small(b2, wp.invpyn), py = b2 - f * wp.pyn;
-      const int y = 16 * py + (r >> 4), x = 16 * px + (r & 15);
+      pf = div_small(b2, wp.invpyn);
+      const int py = b2 - pf * wp.pyn;
+      py0 = 16 * py;
+      px0 = 16 * px;
+      const int y = py0 + (r >> 4), x = px0 + (r & 15);
       qvalid = y < wp.H && x < wp.W;
-      qtok = qvalid ? (f * wp.H + y) * wp.W + x : 0;
+      qtok = qvalid ? (pf * wp.H + y) * wp.W + x : 0;
     } else {
       qtok = qt * BR + r;
       qvalid = qtok < Nq;
@@ -215,21 +222,34 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         if (j <= nt) issue(j, tile_at(j), tile_at(j - 1));
     // grid coordinates of the row, once
     const int hw = rp.H * rp.W;
-    const int cf = rp.enabled ? pos / hw : 0;
-    const int cy = rp.enabled ? (pos - cf * hw) / rp.W : 0;
-    const int cx = pos - cf * hw - cy * rp.W;
-    // Window variant: the cos/sin of every (axis position, pair) of the
-    // grid, once per workgroup, in the ring stage the prologue does not fill
-    // (stage NS-1, first refilled after the barrier that opens tile period
-    // 0): per axis, extent x pairs entries of (cos, sin), t then h then w.
-    // The 256 rows of a workgroup share few positions per axis, so this
-    // evaluates far fewer angles than one per (row, pair), which matters
-    // where a workgroup visits few tiles; the values are those of
-    // rope_angle_cos_sin, so the rotation is the same bit for bit. Grids
-    // whose table does not fit the stage evaluate each lane's angles.
+    int cf, cy, cx;
+    if constexpr (WIN == kWinPatch) {
+      const int r = wave * 32 + qi;
+      cf = pf;
+      cy = py0 + (r >> 4);
+      cx = px0 + (r & 15);
+    } else {
+      cf = rp.enabled ? pos / hw : 0;
+      cy = rp.enabled ? (pos - cf * hw) / rp.W : 0;
+      cx = pos - cf * hw - cy * rp.W;
+    }
+    // Window variants: the cos/sin of every (axis position, pair) the
+    // workgroup's rows can use, once per workgroup, in the ring stage the
+    // prologue does not fill (stage NS-1, first refilled after the barrier
+    // that opens tile period 0): per axis, extent x pairs entries of
+    // (cos, sin), t then h then w, over the whole grid (row layout) or the
+    // patch's frame, 16 rows and 16 columns (patch layout). The 256 rows of
+    // a workgroup share few positions per axis, so this evaluates far fewer
+    // angles than one per (row, pair), which matters where a workgroup
+    // visits few tiles; the values are those of rope_angle_cos_sin, so the
+    // rotation is the same bit for bit. Tables that do not fit the stage
+    // give way to each lane's own angles.
+    constexpr bool kPatch = WIN == kWinPatch;
+    const int f0 = kPatch ? pf : 0, y0 = kPatch ? py0 : 0, x0 = kPatch ? px0 : 0;
+    const int nf = kPatch ? 1 : rp.F, nh = kPatch ? 16 : rp.H, nw = kPatch ? 16 : rp.W;
     const int npt = rp.pair_t, nph = rp.pair_th - rp.pair_t, npw = D / 2 - rp.pair_th;
-    const int base_h = rp.F * npt, base_w = base_h + rp.H * nph, n_ent = base_w + rp.W * npw;
-    const bool table = WIN && NS >= 3 && rp.enabled && n_ent <= STAGE / 8;
+    const int base_h = nf * npt, base_w = base_h + nh * nph, n_ent = base_w + nw * npw;
+    const bool table = WIN != kWinNone && NS >= 3 && rp.enabled && n_ent <= STAGE / 8;
     float2* tbl = reinterpret_cast<float2*>(lds + (NS - 1) * STAGE);
     if (table) {
       for (int e = threadIdx.x; e < n_ent; e += NW * 64) {
@@ -237,12 +257,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         if (e < base_h) {
           apos = e / npt;
           pair = e - apos * npt;
+          apos += f0;
         } else if (e < base_w) {
           apos = (e - base_h) / nph;
           pair = rp.pair_t + (e - base_h - apos * nph);
+          apos += y0;
         } else {
           apos = (e - base_w) / npw;
           pair = rp.pair_th + (e - base_w - apos * npw);
+          apos += x0;
         }
         float c, sn;
         rope_angle_cos_sin(apos, rp.omega[pair], c, sn);
@@ -263,9 +286,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           float c, sn;
           if (table) {
             const int p = g ? p1 : p0;
-            const int e = p < rp.pair_t ? cf * npt + p
-                                        : (p < rp.pair_th ? base_h + cy * nph + (p - rp.pair_t)
-                                                          : base_w + cx * npw + (p - rp.pair_th));
+            const int e = p < rp.pair_t ? (cf - f0) * npt + p
+                                        : (p < rp.pair_th ? base_h + (cy - y0) * nph + (p - rp.pair_t)
+                                                          : base_w + (cx - x0) * npw + (p - rp.pair_th));
             const float2 cs = tbl[e];
             c = cs.x;
             sn = cs.y;
@@ -289,18 +312,33 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   bf16x8 pk[MS];
   float m = 0.f, l = 0.f;
   bool m_valid = false;  // this row's m comes from a visible key
+  // window bits of the tile whose scores the last GEMM phase produced (the
+  // softmax phase that follows reads them; in the patch layout ~0 or 0,
+  // whether the query sees any key of the tile); all keys count as visible
+  // outside the window variants
+  unsigned wvis = ~0u;
   // Window of this lane's query (window variant): a key at (f, y, x) is
   // visible when f - flo, y - ylo and x - clo, as unsigned, are at most
   // 2 r_f, 2 r_h and 2 r_w. For the fast test, a run of 8 keys starting at
   // column c0 of row r0 sees columns [clo, cend) of row r0 and, after the
   // row wrap, [wlo, wend) counted from the run's start as W - c0 + column.
-  int flo = 0, ylo = 0, clo = 0, cend = 0, wlo = 0, wend = 0;
-  if constexpr (WIN) {
-    const int t = qtok;
-    const int hw = wp.H * wp.W;
-    const int qf = t / hw;
-    const int qy = (t - qf * hw) / wp.W;
-    const int qx = t - qf * hw - qy * wp.W;
+  // The patch layout tests rows and columns on their own: this lane's query
+  // sees grid rows [ylo, yend) and columns [clo, cend).
+  int flo = 0, ylo = 0, clo = 0, cend = 0, wlo = 0, wend = 0, yend = 0;
+  if constexpr (WIN != kWinNone) {
+    int qf, qy, qx;
+    if constexpr (WIN == kWinPatch) {
+      const int r = wave * 32 + qi;
+      qf = pf;
+      qy = py0 + (r >> 4);
+      qx = px0 + (r & 15);
+    } else {
+      const int t = qtok;
+      const int hw = wp.H * wp.W;
+      qf = t / hw;
+      qy = (t - qf * hw) / wp.W;
+      qx = t - qf * hw - qy * wp.W;
+    }
     flo = qf - wp.rf;
     ylo = qy - wp.rh;
     clo = qx - wp.rw;
@@ -308,6 +346,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     cend = chi + 1;
     wlo = wp.W + (clo > 0 ? clo : 0);
     wend = wp.W + chi + 1;
+    yend = (qy + wp.rh < wp.H - 1 ? qy + wp.rh : wp.H - 1) + 1;
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) negm[i] = -kBias;
@@ -376,7 +415,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = xor32_max(mx) + kBias;
-    const bool seen = mx > -INFINITY;
+    // (in the patch layout a hidden key's score is finite, and wvis, the
+    // same in both halves of the wave, decides; elsewhere wvis covers only
+    // this lane's half of the tile)
+    const bool seen = WIN == kWinPatch ? wvis != 0u : mx > -INFINITY;
     const float delta = !m_valid ? (seen ? mx : 0.f) : fmaxf(mx, 0.f);
     const float alpha = !m_valid ? 1.f : __builtin_amdgcn_exp2f(-delta);
     m_valid = m_valid || seen;
@@ -399,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   constexpr int kVmcntZero = (0x7 << 4) | (0xF << 8);
   // valid keys of the last key tile, 1..KT (the patch layout's edge keys are
   // masked by the window test instead)
-  const int tail = WIN && wp.mode == 3 ? KT : N - (nkt - 1) * KT;
+  const int tail = WIN == kWinPatch ? KT : N - (nkt - 1) * KT;
 
   // Barrier that opens tile period i: tile i must have landed (a loader's
   // loads of the newer tiles may stay in flight).
@@ -418,27 +460,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // key outside the box) while the matrix core runs the P.V products.
   auto window_vis = [&](int tile) __attribute__((always_inline)) {
     unsigned vis = 0;
-    if constexpr (WIN) {
+    if constexpr (WIN == kWinRows) {
       const int base = tile * KT;
       const unsigned fspan = 2u * wp.rf, yspan = 2u * wp.rh, xspan = 2u * wp.rw;
       const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
-      if (wp.mode == 3) {
-        // patch tile (tf, ty, tx): run u of this lane is patch row 2u + g,
-        // all 8 columns; the columns it sees are the same for every row
-        const int t2 = div_small(tile, wp.invtxn), tx = tile - t2 * wp.txn;
-        const int tf = div_small(t2, wp.invtyn), ty = t2 - tf * wp.tyn;
-        const int x0 = 8 * tx;
-        const int a = clo - x0 < 0 ? 0 : (clo - x0 > 8 ? 8 : clo - x0);
-        const int b = cend - x0 < a ? a : (cend - x0 > 8 ? 8 : cend - x0);
-        const unsigned cm = (1u << b) - (1u << a);
-        const bool fok = (unsigned)(tf - flo) <= fspan;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int y = 8 * ty + 2 * u + g;
-          const bool rok = fok & ((unsigned)(y - ylo) <= yspan) & (y < wp.H);
-          vis |= (rok ? cm : 0u) << (8 * u);
-        }
-      } else if (wp.mode == 2) {
+      if (wp.mode == 2) {
         // the tile [base, base + 64) lies in rows rb and rb + 1; the visible
         // keys of each row form one range of tile offsets
         auto bits64 = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..63
@@ -510,10 +536,51 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     return vis;
   };
 
-  // window bits of the tile whose scores the last GEMM phase produced (the
-  // softmax phase that follows reads them); all keys count as visible
-  // outside the window variant
-  unsigned wvis = ~0u;
+
+  // Patch layout: the box test runs on the matrix core. Key kk of a tile
+  // lies in tile row kk/8 and column kk%8, so an extra score MFMA per key
+  // block, with a one-hot A operand (the key's row among k = 0..7, its
+  // column among k = 8..15) and a B operand of per-query penalties (0 for a
+  // tile row or column the query sees, -3.39e38 for one it does not), turns
+  // the accumulator input -m into exactly -m for a visible key and into at
+  // most -3.39e38 (or -inf) for a hidden one; the score products that follow
+  // (at most 2^40 in size) cannot lift it. Its products are 1 x pen or
+  // 0 x pen, never 0 x inf, so no NaN arises.
+  bf16x8 onehot[2];
+  if constexpr (WIN == kWinPatch) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kk = 32 * kb + rho32(qi);  // the key of A row qi in key block kb
+      const int hot = g ? (kk & 7) : (kk >> 3);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) onehot[kb][j] = (__bf16)(j == hot ? 1.f : 0.f);
+    }
+  }
+  // This lane's half of the penalty operand for tile t (rows for g = 0,
+  // columns for g = 1); sets wvis.
+  auto patch_penalty = [&](int tile) __attribute__((always_inline)) {
+    bf16x8 pen;
+    if constexpr (WIN == kWinPatch) {
+      const int t2 = div_small(tile, wp.invtxn), tx = tile - t2 * wp.txn;
+      const int tf = div_small(t2, wp.invtyn), ty = t2 - tf * wp.tyn;
+      auto bits8 = [](int a, int b) __attribute__((always_inline)) {  // bits [a, b) of 0..7
+        const int lo = a < 0 ? 0 : (a > 8 ? 8 : a);
+        const int hi = b < lo ? lo : (b > 8 ? 8 : b);
+        return (1u << hi) - (1u << lo);
+      };
+      const unsigned rows = bits8(ylo - 8 * ty, yend - 8 * ty);
+      const unsigned cols = bits8(clo - 8 * tx, cend - 8 * tx);
+      const bool fok = (unsigned)(tf - flo) <= 2u * wp.rf;
+      wvis = fok && rows != 0u && cols != 0u ? ~0u : 0u;
+      const unsigned hide = fok ? ~(g ? cols : rows) : ~0u;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)  // bf16 0xFF7F = -3.39e38 for a hidden row or column
+        w[e] = (((hide >> (2 * e)) & 1u) | (((hide >> (2 * e + 1)) & 1u) << 16)) * 0xFF7Fu;
+      pen = __builtin_bit_cast(bf16x8, w);
+    }
+    return pen;
+  };
 
   // Workspace tiles of loop tiles j-1 .. j+NS-1 in tile period j:
   // tw[k] = tile_at(j - 1 + k). Each period reads one list entry, for the
@@ -577,10 +644,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     constexpr int NB = NOP / RB;
     // scheduling groups that keep the batch structure of batches b0 .. b1:
     // the reads of batch b + 1, then the MFMAs of batch b
+    // (the patch layout's box MFMAs join the batch of the first K operand)
+    constexpr bool kBox = WIN == kWinPatch && decltype(SC)::value;
     auto groups = [&](int b0, int b1) __attribute__((always_inline)) {
       for (int b = b0; b <= b1; ++b) {
         if (b + 1 < NB) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);                // MFMA
+        if (kBox && b == NV / RB)
+          __builtin_amdgcn_sched_group_barrier(0x008, RB + 2, 0);  // MFMA
+        else
+          __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
       }
     };
     // Operand i < NV is V block vb(i) = (db, ms), else K block kbs(i - NV) =
@@ -594,7 +666,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     // accumulator input of the first score MFMA per key block: -m, or -inf
     // for a key outside the window (sign-extended bit, then a bit select)
     f32x16 cneg[2];
-    if constexpr (WIN && decltype(SC)::value) {
+    bf16x8 pen;
+    if constexpr (kBox) pen = patch_penalty(tw[1]);
+    if constexpr (WIN == kWinRows && decltype(SC)::value) {
       const unsigned vis = window_vis(tw[1]);
       wvis = vis;
 #pragma unroll
@@ -625,8 +699,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pk[ms], oacc[db], 0, 0, 0);
         } else {
           const int kb = kbs(i - NV) / KSTEPS, s = kbs(i - NV) % KSTEPS;
+          if constexpr (kBox) {
+            if (i == NV) {
+#pragma unroll
+              for (int k2 = 0; k2 < 2; ++k2)
+                sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(onehot[k2], pen, negm, 0, 0, 0);
+            }
+          }
+          const f32x16 c0 = WIN == kWinPatch ? sacc[kb] : (WIN == kWinRows ? cneg[kb] : negm);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), qreg[s],
-                                                            s == 0 ? (WIN ? cneg[kb] : negm) : sacc[kb], 0, 0, 0);
+                                                            s == 0 ? c0 : sacc[kb], 0, 0, 0);
         }
       }
     }

@@ -365,11 +365,12 @@ struct AttendExtras {
   int maxb = 0;
   int lists_shared = 0;  // one list per query block for every (b, head)
   bool window = false;   // mask keys outside each query's box
+  bool patch = false;    // ... in the patch layout (else the row layout)
   WindowParams wp{1, 1, 1, 0, 0, 0, 0, 1.f, 1.f, 1, 1, 1, 1, 1.f, 1.f, 1.f, 1.f};
   int64_t nkt = 0, ntq = 0;  // > 0: key tiles and query blocks of the patch layout
 };
 
-template <int D, bool SPARSE, bool WIN>
+template <int D, bool SPARSE, int WIN>
 void launch_bf16(const void* q, const uint8_t* ws, void* o, int N, int nkt, int Nq, int ntq, int total, float qscale,
                  const RopeParams& rp, const AttendExtras& x, hipStream_t st) {
   hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<D, VIDATTN_BF16_NS, SPARSE, WIN>), dim3((unsigned)total),
@@ -390,20 +391,25 @@ vidattn_status launch_attend(const void* q, const void* k, const void* v, const 
     const uint8_t* ws = static_cast<const uint8_t*>(workspace);
     const bool sparse = x.kvb != nullptr;
     const int n = (int)N, nq = (int)Nq;
+    const bool patch = x.window && x.patch;
     if (d == 128) {
-      if (x.window)
-        launch_bf16<128, true, true>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+      if (patch)
+        launch_bf16<128, true, kWinPatch>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+      else if (x.window)
+        launch_bf16<128, true, kWinRows>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
       else if (sparse)
-        launch_bf16<128, true, false>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+        launch_bf16<128, true, kWinNone>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
       else
-        launch_bf16<128, false, false>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+        launch_bf16<128, false, kWinNone>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
     } else {
-      if (x.window)
-        launch_bf16<64, true, true>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+      if (patch)
+        launch_bf16<64, true, kWinPatch>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+      else if (x.window)
+        launch_bf16<64, true, kWinRows>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
       else if (sparse)
-        launch_bf16<64, true, false>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+        launch_bf16<64, true, kWinNone>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
       else
-        launch_bf16<64, false, false>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
+        launch_bf16<64, false, kWinNone>(q, ws, o, n, nkt, nq, ntq, total, qscale, rp, x, st);
     }
     return hip_check("bf16 attention launch");
   }
@@ -673,9 +679,9 @@ vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, v
   x.maxb = (int)g.nkt;
   x.lists_shared = 1;
   x.window = true;
-  int mode;
+  int mode = 0;  // the row layout's key decode (the patch layout has its own)
   if (patch) {
-    mode = 3;
+    x.patch = true;
     x.nkt = g.nkt;
     x.ntq = g.nqb;
   } else {
