@@ -556,10 +556,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       for (int j = 0; j < 8; ++j) onehot[kb][j] = (__bf16)(j == hot ? 1.f : 0.f);
     }
   }
-  // This lane's half of the penalty operand for tile t (rows for g = 0,
-  // columns for g = 1); sets wvis.
-  auto patch_penalty = [&](int tile) __attribute__((always_inline)) {
-    bf16x8 pen;
+  // The penalty operand of the tile the next score product covers (this
+  // lane's half: rows for g = 0, columns for g = 1) and whether the lane's
+  // query sees any of its keys (it becomes wvis once the scores exist).
+  bf16x8 pen_sc;
+  unsigned vis_sc = ~0u;
+  // Sets pen_sc and vis_sc for tile t and returns whether any query of the
+  // wave sees a key of it. A wave that sees none skips the tile's score
+  // product, softmax and P.V product: its probabilities would all be 0, so
+  // the result is the same bit for bit. Outside the patch layout every tile
+  // is needed (a constant, so the skips compile away).
+  auto prep_scores = [&](int tile) __attribute__((always_inline)) -> bool {
     if constexpr (WIN == kWinPatch) {
       const int t2 = div_small(tile, wp.invtxn), tx = tile - t2 * wp.txn;
       const int tf = div_small(t2, wp.invtyn), ty = t2 - tf * wp.tyn;
@@ -571,15 +578,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       const unsigned rows = bits8(ylo - 8 * ty, yend - 8 * ty);
       const unsigned cols = bits8(clo - 8 * tx, cend - 8 * tx);
       const bool fok = (unsigned)(tf - flo) <= 2u * wp.rf;
-      wvis = fok && rows != 0u && cols != 0u ? ~0u : 0u;
+      vis_sc = fok && rows != 0u && cols != 0u ? ~0u : 0u;
       const unsigned hide = fok ? ~(g ? cols : rows) : ~0u;
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e)  // bf16 0xFF7F = -3.39e38 for a hidden row or column
         w[e] = (((hide >> (2 * e)) & 1u) | (((hide >> (2 * e + 1)) & 1u) << 16)) * 0xFF7Fu;
-      pen = __builtin_bit_cast(bf16x8, w);
+      pen_sc = __builtin_bit_cast(bf16x8, w);
+      return __builtin_amdgcn_ballot_w64(vis_sc != 0u) != 0;
+    } else {
+      (void)tile;
+      return true;
     }
-    return pen;
   };
 
   // Workspace tiles of loop tiles j-1 .. j+NS-1 in tile period j:
@@ -666,8 +676,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     // accumulator input of the first score MFMA per key block: -m, or -inf
     // for a key outside the window (sign-extended bit, then a bit select)
     f32x16 cneg[2];
-    bf16x8 pen;
-    if constexpr (kBox) pen = patch_penalty(tw[1]);
+    if constexpr (kBox) wvis = vis_sc;
     if constexpr (WIN == kWinRows && decltype(SC)::value) {
       const unsigned vis = window_vis(tw[1]);
       wvis = vis;
@@ -703,7 +712,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
             if (i == NV) {
 #pragma unroll
               for (int k2 = 0; k2 < 2; ++k2)
-                sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(onehot[k2], pen, negm, 0, 0, 0);
+                sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(onehot[k2], pen_sc, negm, 0, 0, 0);
             }
           }
           const f32x16 c0 = WIN == kWinPatch ? sacc[kb] : (WIN == kWinRows ? cneg[kb] : negm);
@@ -765,11 +774,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   auto prefetch = [&](int i) __attribute__((always_inline)) {
     if constexpr (SPARSE) tnext = tile_at(i + NS);
   };
-  auto sm = [&](auto FILL, int t, int fill_tile, int i, auto SUM) __attribute__((always_inline)) {
+  // (scores: the wave needs tile t; else its probabilities are set to 0,
+  // which is what the softmax would give, so a P.V product that still runs
+  // adds exact zeros)
+  auto sm = [&](auto FILL, int t, int fill_tile, int i, auto SUM, bool scores) __attribute__((always_inline)) {
     if constexpr (SPARSE) __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(FILL)::value) issue(fill_tile, tile_k(NS, i), tile_k(NS - 1, i));
     prefetch(i);
-    softmax(t, SUM);
+    if (scores) {
+      softmax(t, SUM);
+    } else {
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) pk[ms] = bf16x8{};
+    }
   };
   // before a GEMM phase that no barrier precedes: no list read in flight
   auto lists_landed = [&]() __attribute__((always_inline)) {
@@ -782,29 +799,45 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   };
   const Batch nob{};
   tile_barrier(0);
+  // Patch layout: a wave skips a tile none of its queries sees. pv: the wave
+  // needs the tile whose probabilities are in pk (its P.V product is still
+  // to come); sc: it needs the tile of this period's score product. A GEMM
+  // phase runs when either holds (the other half then multiplies zeros or
+  // scores a hidden tile); a softmax runs when its tile is needed. need()
+  // makes every test constant outside the patch layout.
+  auto need = [](bool b) __attribute__((always_inline)) { return WIN != kWinPatch || b; };
+  bool pv = false;
   if (group == 0) {  // period i: GEMM_i then SOFTMAX_i (with the row sums)
     if (NS - 1 <= nt) {
-      gemm(F{}, T{}, 0, F{}, F{}, nob);
-      sm(T{}, tile_k(1, 0), NS - 1, 0, T{});
+      const bool sc = prep_scores(tile_k(1, 0));
+      if (need(sc)) gemm(F{}, T{}, 0, F{}, F{}, nob);
+      sm(T{}, tile_k(1, 0), NS - 1, 0, T{}, need(sc));
+      pv = sc;
     } else {
-      gemm(F{}, T{}, 0, F{}, F{}, nob);
-      sm(F{}, tile_k(1, 0), 0, 0, T{});
+      const bool sc = prep_scores(tile_k(1, 0));
+      if (need(sc)) gemm(F{}, T{}, 0, F{}, F{}, nob);
+      sm(F{}, tile_k(1, 0), 0, 0, T{}, need(sc));
+      pv = sc;
     }
     int j = 1;
     for (; j < nt && j + NS - 1 <= nt; ++j) {
       advance();
       tile_barrier(j);
-      gemm(T{}, T{}, j, F{}, F{}, nob);
-      sm(T{}, tile_k(1, j), j + NS - 1, j, T{});
+      const bool sc = prep_scores(tile_k(1, j));
+      if (need(pv || sc)) gemm(T{}, T{}, j, F{}, F{}, nob);
+      sm(T{}, tile_k(1, j), j + NS - 1, j, T{}, need(sc));
+      pv = sc;
     }
     for (; j < nt; ++j) {
       advance();
       tile_barrier(j);
-      gemm(T{}, T{}, j, F{}, F{}, nob);
-      sm(F{}, tile_k(1, j), 0, j, T{});
+      const bool sc = prep_scores(tile_k(1, j));
+      if (need(pv || sc)) gemm(T{}, T{}, j, F{}, F{}, nob);
+      sm(F{}, tile_k(1, j), 0, j, T{}, need(sc));
+      pv = sc;
     }
     tile_barrier(nt);
-    gemm(T{}, F{}, nt, F{}, F{}, nob);
+    if (need(pv)) gemm(T{}, F{}, nt, F{}, F{}, nob);
   } else {  // period i: SOFTMAX_{i-1} then GEMM_i (period 0: GEMM_0 only)
     // Group B's softmax is the longer path through a period: it reads its
     // first GEMM operands before it, and leaves its row sums to the GEMM
@@ -815,13 +848,28 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     }
     prefetch(0);
     lists_landed();
-    gemm(F{}, T{}, 0, F{}, F{}, nob);
+    {
+      const bool sc = prep_scores(tile_k(1, 0));
+      if (need(sc)) gemm(F{}, T{}, 0, F{}, F{}, nob);
+      pv = sc;
+    }
     int j = 1;
     auto period_b = [&](int jj) __attribute__((always_inline)) {
-      const Batch pre = first_batch(jj);
-      sm(F{}, tile_k(0, jj), 0, jj, F{});
-      lists_landed();
-      gemm(T{}, T{}, jj, T{}, T{}, pre);
+      if constexpr (WIN == kWinPatch) {
+        const bool sc = prep_scores(tile_k(1, jj));
+        const bool run = pv || sc;
+        Batch pre{};
+        if (run) pre = first_batch(jj);
+        sm(F{}, tile_k(0, jj), 0, jj, F{}, pv);
+        lists_landed();
+        if (run) gemm(T{}, T{}, jj, T{}, T{}, pre);
+        pv = sc;
+      } else {
+        const Batch pre = first_batch(jj);
+        sm(F{}, tile_k(0, jj), 0, jj, F{}, true);
+        lists_landed();
+        gemm(T{}, T{}, jj, T{}, T{}, pre);
+      }
     };
     if constexpr (kFillB) {
       for (; j < nt && j + NS - 1 <= nt; ++j) {
@@ -839,9 +887,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     }
     advance();
     tile_barrier(nt);
-    const Batch pre = first_batch(nt);
-    softmax(tile_k(0, nt), F{});
-    gemm(T{}, F{}, nt, T{}, T{}, pre);
+    if (need(pv)) {
+      const Batch pre = first_batch(nt);
+      softmax(tile_k(0, nt), F{});
+      gemm(T{}, F{}, nt, T{}, T{}, pre);
+    }
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16.
