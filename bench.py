@@ -70,11 +70,13 @@ def committed_summary(pattern: str, workload_name: str, kernel: str, keys) -> di
     return None
 
 
-def profile_block(workload_name: str, kernel: str, kernel_ms: float) -> tuple:
+def profile_block(workload_name: str, kernel: str, kernel_ms: float, this_run: str = "kernel") -> tuple:
     """(traffic bytes per launch or None, the 'profile' block of the roofline):
     counters of separate rocprofv3 runs on the same kernel source, labelled
     with their file and the kernel time in those runs, which may have been on
-    another board (boards of this GPU differ by several per cent)."""
+    another board (boards of this GPU differ by several per cent). kernel_ms
+    is this run's time of the kernel (this_run="kernel") or of the whole call
+    it sits in (this_run="call")."""
     tr = committed_summary("*traffic*.md", workload_name, kernel, ("traffic_bytes_per_launch",))
     ct = committed_summary("*counters*.md", workload_name, kernel, ("mfma_busy_frac", "clock_ghz"))
     block = {}
@@ -90,7 +92,7 @@ def profile_block(workload_name: str, kernel: str, kernel_ms: float) -> tuple:
             if k in ct:
                 block[{"kernel_ms": "counters_run_kernel_ms"}.get(k, k)] = ct[k]
     if block:
-        block["this_run_kernel_ms"] = round(kernel_ms, 3)
+        block[f"this_run_{this_run}_ms"] = round(kernel_ms, 3)
         block["note"] = ("counters from separate rocprofv3 runs of the same kernel source (files above); "
                          "achieved and frac are this run's")
     return traffic, (block or None)
@@ -409,6 +411,10 @@ def variant_bench(args, va, wl, host, q, k, v, ws, rope, stream) -> int:
         "roofline": {"kernel": KERNEL, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
     }
+    traffic, prof = profile_block(name, KERNEL, attn_mean)
+    result["roofline"]["traffic"] = traffic
+    if prof:
+        result["roofline"]["profile"] = prof
     if mask_path is not None:
         result["bit_mask_path"] = mask_path
     if not args.no_parity:
@@ -649,6 +655,12 @@ def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
                      "visited_achieved": round(tflops(flops, ms), 2),
                      "visited_frac": round(tflops(flops, ms) / PEAK_TFLOPS, 4)},
     }
+    # the attention kernel's own traffic and counters (committed summaries of
+    # this kernel source), beside this run's whole-call time
+    traffic, prof = profile_block(result["config"]["workload"], KERNEL, ms, this_run="call")
+    result["roofline"]["traffic"] = traffic
+    if prof:
+        result["roofline"]["profile"] = prof
     if not args.no_parity:
         from threadpoolctl import threadpool_limits
         worst = dict(max_abs=0.0, mean_rel=0.0)
