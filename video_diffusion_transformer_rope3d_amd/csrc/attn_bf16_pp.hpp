@@ -44,9 +44,9 @@
 // shared by every (b, head) (lists_shared). Local window (WIN != kWinNone,
 // on top of SPARSE): in the listed tiles, keys outside the box of radii
 // (r_f, r_h, r_w) around the query's grid position get -inf (row layout) or
-// a score below -3e38 (patch layout), which exp2 takes to 0 all the same. Indices read from device
-// memory are clamped into range, so no input can address outside the
-// workspace. A row's m is unset until its first tile with a visible key
+// a score below -3e38 (patch layout), which exp2 takes to 0 all the same.
+// Indices read from device memory are clamped into range, so no input can
+// address outside the workspace. A row's m is unset until its first tile with a visible key
 // (in the dense case: the first tile); the exact step runs on that tile, so
 // tiles whose keys are all masked for a row leave its m untouched.
 #pragma once
@@ -535,7 +535,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     }
     return vis;
   };
-
 
   // Patch layout: the box test runs on the matrix core. Key kk of a tile
   // lies in tile row kk/8 and column kk%8, so an extra score MFMA per key
