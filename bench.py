@@ -624,7 +624,8 @@ def window_bench(args, va, wl, host, q, k, v, rope, stream) -> int:
     nqb = len(want)
     nkt = (wl.N + 63) // 64 if layout == "rows" else wl.grid[0] * -(-wl.grid[1] // 8) * -(-wl.grid[2] // 8)
     base = 256 * wl.d * wl.B * wl.heads * nkt  # the key/value image comes first
-    if n != base + (4 * nqb + 255) // 256 * 256 + 4 * nqb * nkt:
+    # then the counts, and lists as wide as the most tiles a block lists
+    if n != base + (4 * nqb + 255) // 256 * 256 + 4 * nqb * max(want):
         raise RuntimeError(f"window workspace size does not match the {layout} layout")
     if args.warmup > 0:
         got = wws[base:base + 4 * nqb].view(torch.int32).cpu().tolist()

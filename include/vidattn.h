@@ -319,10 +319,12 @@ vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, v
 /* Workspace bytes vidattn_fwd_window needs for this window (its layout, as
  * resolved for VIDATTN_WINDOW_AUTO): the key/value image of nkt key tiles per
  * (b, head), 256*d*B*heads*nkt bytes, then a 256-byte-padded count array of
- * nqb entries and the tile lists, 4*nqb*nkt bytes. Rows: nkt = ceil(N/64),
- * nqb = ceil(N/256) (the image is vidattn_fwd_workspace_size bytes);
- * patches: nkt = F*ceil(H/8)*ceil(W/8), nqb = F*ceil(H/16)*ceil(W/16).
- * 0 for arguments vidattn_fwd_window would reject by dtype, size or window. */
+ * nqb entries and the tile lists, 4*nqb*cap bytes, where cap is the most key
+ * tiles any query block lists (found on the host from the grid and radii).
+ * Rows: nkt = ceil(N/64), nqb = ceil(N/256) (the image is
+ * vidattn_fwd_workspace_size bytes); patches: nkt = F*ceil(H/8)*ceil(W/8),
+ * nqb = F*ceil(H/16)*ceil(W/16). 0 for arguments vidattn_fwd_window would
+ * reject by dtype, size or window. */
 size_t vidattn_fwd_window_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
                                          int use_rope, const vidattn_window_desc* window);
 

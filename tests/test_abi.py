@@ -234,15 +234,27 @@ def test_block_mask_words_layout():
 
 
 def test_window_rejects_and_sizes():
+    """Sizes: the key/value image, the counts, and lists as wide as the most
+    tiles a block lists (the rules restated in bench.py give those counts)."""
+    import importlib.util
+    import os
+    import workloads as wlmod
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_module", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    wl = wlmod.custom(2, 40, (21, 45, 80), 128, (44, 42, 42))
     base = va.vidattn_fwd_workspace_size(va.BF16, 2, 40, N5, 128, 1)
     W = va.WindowDesc.make((21, 45, 80), (1, 4, 4), "rows")
     wsb = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1, W)
-    nqb, nkt = -(-N5 // 256), -(-N5 // 64)
-    assert wsb == base + (nqb * 4 + 255) // 256 * 256 + nqb * nkt * 4
+    nqb, cap = -(-N5 // 256), max(bench.window_plan_counts(wl, (1, 4, 4), "rows"))
+    assert wsb == base + (nqb * 4 + 255) // 256 * 256 + nqb * cap * 4
     WP = va.WindowDesc.make((21, 45, 80), (1, 4, 4), "patches")
     wsp = va.vidattn_fwd_window_workspace_size(va.BF16, 2, 40, N5, 128, 1, WP)
     pqb, pkt = 21 * 3 * 5, 21 * 6 * 10
-    assert wsp == 2 * 40 * 256 * 128 * pkt + (pqb * 4 + 255) // 256 * 256 + pqb * pkt * 4
+    pcap = max(bench.window_plan_counts(wl, (1, 4, 4), "patches"))
+    assert pcap == 3 * 4 * 4
+    assert wsp == 2 * 40 * 256 * 128 * pkt + (pqb * 4 + 255) // 256 * 256 + pqb * pcap * 4
     assert va.vidattn_fwd_window_workspace_size(va.F32, 2, 40, N5, 128, 1, W) == 0
     win = lambda **kw: va.vidattn_fwd_window(**{**dict(
         q=QF, k=QF + T // 4, v=QF + T // 2, o=OF, dt=va.BF16, B=2, heads=40, N=N5, d=128, softmax_scale=0.1,

@@ -462,9 +462,11 @@ def test_window_plan_kernel_writes_the_rule(va, layout):
             nqb, nkt = F * -(-H // 16) * -(-W // 16), F * -(-H // 8) * -(-W // 8)
             want = bench.window_patch_lists(wl, radius)
         base = 256 * wl.d * nkt  # the key/value image of one (b, head)
+        cap = max(len(t) for t in want)  # list rows are as wide as the longest list
+        assert n == base + (4 * nqb + 255) // 256 * 256 + 4 * nqb * cap, (grid, radius)
         counts = ws[base:base + 4 * nqb].view(torch.int32).cpu().tolist()
         off = base + (4 * nqb + 255) // 256 * 256
-        lists = ws[off:off + 4 * nqb * nkt].view(torch.int32).view(nqb, nkt).cpu().tolist()
+        lists = ws[off:off + 4 * nqb * cap].view(torch.int32).view(nqb, cap).cpu().tolist()
         got = [row[:c] for row, c in zip(lists, counts)]
         assert got == want, (grid, radius)
 

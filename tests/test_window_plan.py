@@ -138,16 +138,17 @@ def test_library_picks_the_layout_that_lists_fewer_tiles():
     must give that layout's size."""
     import video_diffusion_transformer_rope3d_amd as va
 
-    def size(nqb, nkt, d=64):
-        return 256 * d * nkt + (4 * nqb + 255) // 256 * 256 + 4 * nqb * nkt
+    def size(nqb, nkt, cap, d=64):  # the image, the counts, lists of cap entries per block
+        return 256 * d * nkt + (4 * nqb + 255) // 256 * 256 + 4 * nqb * cap
 
     cases = PATCH_CASES + [((21, 45, 80), r) for r in ((1, 7, 7), (1, 3, 3), (0, 0, 80), (2, 1, 1), (21, 45, 80))]
     picked = set()
     for grid, radius in cases:
         wl = wlmod.custom(1, 1, grid, 64, (16, 24, 24))
         F, H, W = grid
-        rows = size(-(-wl.N // 256), -(-wl.N // 64))
-        patches = size(F * -(-H // 16) * -(-W // 16), F * -(-H // 8) * -(-W // 8))
+        rows = size(-(-wl.N // 256), -(-wl.N // 64), max(bench.window_plan_counts(wl, radius, "rows")))
+        patches = size(F * -(-H // 16) * -(-W // 16), F * -(-H // 8) * -(-W // 8),
+                       max(bench.window_plan_counts(wl, radius, "patches")))
         want = bench.window_layout(wl, radius)
         picked.add(want)
         got = {lay: va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, wl.N, 64, True,
@@ -165,3 +166,35 @@ def test_window_size_query_rejects_a_bad_window():
     for bad in (None, va.WindowDesc.make((2, 3, 5), (1, 1, 1)), va.WindowDesc.make((2, 3, 4), (1, -1, 1)),
                 va.WindowDesc.make((2, 3, 4), (1, 1, 1), 3)):
         assert va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, 24, 64, True, bad) == 0
+
+
+def test_auto_layout_falls_back_to_rows_past_the_patch_limit():
+    """A grid of 2^22 or more key patches cannot take the patch layout: the
+    automatic choice gives the row layout's workspace there, and a forced
+    patch layout is refused (size 0). Lists hold as many entries per block
+    as the most any block lists, so even these 2^24-token grids need lists
+    of a few MB, not of N^2/4096 entries."""
+    import video_diffusion_transformer_rope3d_amd as va
+    N = 1 << 24
+    grid = (1 << 16, 1, 256)  # 2^16 * 1 * 32 = 2^21 key patches: still allowed
+    ok = va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, N, 64, False, va.WindowDesc.make(grid, (0, 0, 1), "patches"))
+    # one frame, one tile row, and columns 16p-1 .. 16p+16: tiles 2p-1 .. 2p+2, 4 at most
+    nqb, cap = (1 << 16) * 16, 4
+    assert ok == 256 * 64 * (1 << 16) * 32 + (4 * nqb + 255) // 256 * 256 + 4 * nqb * cap
+    grid = (1 << 24, 1, 1)  # 2^24 key patches
+    # rows: a block's 256 one-token frames, radius 0 in frames: the block's own 4 tiles
+    rows = 256 * 64 * (N // 64) + (4 * (N // 256) + 255) // 256 * 256 + 4 * (N // 256) * 4
+    assert va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, N, 64, False,
+                                                va.WindowDesc.make(grid, (0, 0, 1), "auto")) == rows
+    assert va.vidattn_fwd_window_workspace_size(va.BF16, 1, 1, N, 64, False,
+                                                va.WindowDesc.make(grid, (0, 0, 1), "patches")) == 0
+
+
+@pytest.mark.parametrize("grid", [(2, 16, 32), (3, 33, 18), (1, 7, 5), (21, 45, 80)], ids=lambda g: "x".join(map(str, g)))
+def test_block_rows_cover_every_token_once(grid):
+    """The query rows bench.py counts per block (for the visited-pair FLOPs)
+    add up to N in both layouts, and a patch never counts more than 256."""
+    wl = wlmod.custom(1, 1, grid, 64, (16, 24, 24))
+    for layout in ("rows", "patches"):
+        rows = bench.window_block_rows(wl, layout)
+        assert sum(rows) == wl.N and max(rows) <= 256 and min(rows) >= 1

@@ -532,39 +532,56 @@ static size_t block_mask_list_bytes(int64_t nbh, int64_t N) {
 // Layout of one local-window call and its tile counts (see
 // vidattn_window_desc and window_plan.hpp). Its workspace: the key/value
 // image of nkt tiles per (b, head), then the per-query-block tile counts
-// (padded to 256 bytes), then the tile lists (nqb rows of nkt entries).
+// (padded to 256 bytes), then the tile lists (nqb rows of cap entries, cap
+// the most tiles any block lists, so the lists grow with N, not N^2).
 struct WindowGeom {
   int layout = VIDATTN_WINDOW_ROWS;
   int64_t nkt = 0, nqb = 0;          // key tiles per (b, head), query blocks
+  int64_t cap = 1;                   // entries per list row
   int tyn = 1, txn = 1, pyn = 1, pxn = 1;  // patch counts per axis (patch layout)
   int rf = 0, rh = 0, rw = 0;        // radii clipped to the grid
 };
 
-// Key tiles the row layout lists in all (host count of window_plan_kernel).
-static int64_t rows_tiles_listed(int64_t N, int F, int H, int W, int rf, int rh) {
+// Key tiles a layout lists: in all, and the most for one query block.
+struct TileCount {
+  int64_t total = 0, most = 0;
+};
+
+// The row layout (host count of window_plan_kernel's lists).
+static TileCount rows_tiles_listed(int64_t N, int F, int H, int W, int rf, int rh) {
   const int nqb = (int)((N + kBR - 1) / kBR);
-  int64_t total = 0;
-  for (int i = 0; i < nqb; ++i)
-    window_rows_plan(i, (int)N, F, H, W, rf, rh, [&](int t0, int t1) { total += t1 - t0 + 1; });
-  return total;
+  TileCount c;
+  for (int i = 0; i < nqb; ++i) {
+    int64_t n = 0;
+    window_rows_plan(i, (int)N, F, H, W, rf, rh, [&](int t0, int t1) { n += t1 - t0 + 1; });
+    c.total += n;
+    c.most = std::max(c.most, n);
+  }
+  return c;
 }
 
-// Key tiles the patch layout lists in all: the count of patch (f, py, px) is
-// the product of its frame, row and column spans, so the sum factors.
-static int64_t patch_tiles_listed(const WindowGeom& g, int F, int H, int W) {
-  int64_t sf = 0, sy = 0, sx = 0;
-  for (int f = 0; f < F; ++f) sf += std::min(F - 1, f + g.rf) - std::max(0, f - g.rf) + 1;
+// The patch layout: the count of patch (f, py, px) is the product of its
+// frame, row and column spans, so the sum and the maximum factor.
+static TileCount patch_tiles_listed(const WindowGeom& g, int F, int H, int W) {
+  int64_t sf = 0, sy = 0, sx = 0, mf = 0, my = 0, mx = 0;
+  for (int f = 0; f < F; ++f) {
+    const int64_t n = std::min(F - 1, f + g.rf) - std::max(0, f - g.rf) + 1;
+    sf += n;
+    mf = std::max(mf, n);
+  }
   for (int p = 0; p < g.pyn; ++p) {
     int lo, hi;
     window_patch_span(p, H, g.rh, lo, hi);
     sy += hi - lo + 1;
+    my = std::max<int64_t>(my, hi - lo + 1);
   }
   for (int p = 0; p < g.pxn; ++p) {
     int lo, hi;
     window_patch_span(p, W, g.rw, lo, hi);
     sx += hi - lo + 1;
+    mx = std::max<int64_t>(mx, hi - lo + 1);
   }
-  return sf * sy * sx;
+  return TileCount{sf * sy * sx, mf * my * mx};
 }
 
 // Checks the window against N and rope and resolves its layout.
@@ -595,7 +612,6 @@ static vidattn_status window_geom(const vidattn_window_desc* w, int64_t N, const
   const bool patch_ok = pnkt < (int64_t(1) << 22) && pnqb < (int64_t(1) << 22);
   if (w->layout == VIDATTN_WINDOW_PATCHES && !patch_ok)
     return fail(VIDATTN_ERR_UNSUPPORTED, "patch layout needs fewer than 2^22 key and query patches");
-  if (w->layout == VIDATTN_WINDOW_ROWS || !patch_ok) return VIDATTN_OK;
   WindowGeom p = *g;
   p.layout = VIDATTN_WINDOW_PATCHES;
   p.nkt = pnkt;
@@ -604,10 +620,16 @@ static vidattn_status window_geom(const vidattn_window_desc* w, int64_t N, const
   p.txn = txn;
   p.pyn = pyn;
   p.pxn = pxn;
-  // every listed tile costs the same (256 queries x 64 keys) in both layouts
-  if (w->layout == VIDATTN_WINDOW_PATCHES ||
-      patch_tiles_listed(p, F, H, W) < rows_tiles_listed(N, F, H, W, g->rf, g->rh))
+  const TileCount pc = patch_ok && w->layout != VIDATTN_WINDOW_ROWS ? patch_tiles_listed(p, F, H, W) : TileCount{};
+  p.cap = pc.most;
+  if (w->layout == VIDATTN_WINDOW_PATCHES) {
     *g = p;
+    return VIDATTN_OK;
+  }
+  const TileCount rc = rows_tiles_listed(N, F, H, W, g->rf, g->rh);
+  g->cap = rc.most;
+  // every listed tile costs the same (256 queries x 64 keys) in both layouts
+  if (w->layout == VIDATTN_WINDOW_AUTO && patch_ok && pc.total < rc.total) *g = p;
   return VIDATTN_OK;
 }
 
@@ -616,7 +638,7 @@ static size_t window_image_bytes(int64_t nbh, int64_t d, const WindowGeom& g) {
   return (size_t)(4 * nbh * g.nkt * kKT * d);
 }
 static size_t window_plan_bytes(const WindowGeom& g) {
-  return (size_t)((g.nqb * 4 + 255) / 256 * 256 + g.nqb * g.nkt * 4);
+  return (size_t)((g.nqb * 4 + 255) / 256 * 256 + g.nqb * g.cap * 4);
 }
 
 size_t vidattn_fwd_window_workspace_size(vidattn_dtype dt, int64_t B, int64_t heads, int64_t N, int64_t d,
@@ -667,16 +689,16 @@ vidattn_status vidattn_fwd_window(const void* q, const void* k, const void* v, v
   int32_t* kvb = reinterpret_cast<int32_t*>(tail + (g.nqb * 4 + 255) / 256 * 256);
   const dim3 pgrid((unsigned)((g.nqb + 255) / 256));
   if (patch)
-    hipLaunchKernelGGL(window_plan_patch_kernel, pgrid, dim3(256), 0, st, kvb, kvc, (int)g.nqb, (int)g.nkt, F, H, W,
+    hipLaunchKernelGGL(window_plan_patch_kernel, pgrid, dim3(256), 0, st, kvb, kvc, (int)g.nqb, (int)g.cap, F, H, W,
                        g.rf, g.rh, g.rw, g.tyn, g.txn, g.pyn, g.pxn);
   else
-    hipLaunchKernelGGL(window_plan_kernel, pgrid, dim3(256), 0, st, kvb, kvc, (int)N, (int)g.nqb, (int)g.nkt, F, H,
+    hipLaunchKernelGGL(window_plan_kernel, pgrid, dim3(256), 0, st, kvb, kvc, (int)N, (int)g.nqb, (int)g.cap, F, H,
                        W, g.rf, g.rh);
   if (vidattn_status s = hip_check("window plan launch")) return s;
   AttendExtras x;
   x.kvb = kvb;
   x.kvc = kvc;
-  x.maxb = (int)g.nkt;
+  x.maxb = (int)g.cap;
   x.lists_shared = 1;
   x.window = true;
   int mode = 0;  // the row layout's key decode (the patch layout has its own)

@@ -66,7 +66,7 @@ __host__ __device__ inline void window_rows_plan(int i, int N, int F, int H, int
 }
 
 // One thread per query block i: kv_count[i] and kv_blocks[i*cap ..] (ascending,
-// at most cap entries; cap >= the number of key tiles).
+// at most cap entries; the host sets cap to the most tiles any block lists).
 __global__ __launch_bounds__(256) void window_plan_kernel(int32_t* __restrict__ kv_blocks,
                                                           int32_t* __restrict__ kv_count, int N, int nqb, int cap,
                                                           int F, int H, int W, int rf, int rh) {
