@@ -353,3 +353,36 @@ def test_noalloc_rejects_before_any_device_work():
     assert s == 2 and "head dim" in va.vidattn_last_error()
     s = va.vidattn_fwd_noalloc(None, KF, VF, OF, va.BF16, 2, 40, N5, 128, 0.1, GOOD)
     assert s == 3  # the size check comes first for this shape
+
+
+def test_header_compiles_as_c_and_matches_the_binding_layouts(tmp_path):
+    """include/vidattn.h is a C header: it compiles as pedantic C99, and the
+    size and field offsets of each descriptor struct equal those of the
+    binding's ctypes structures (and the layout constants agree)."""
+    import ctypes
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "vidattn.h"\n'
+        "int main(void) {\n"
+        '  printf("%zu %zu %zu %zu %zu\\n", sizeof(vidattn_rope3d_desc), offsetof(vidattn_rope3d_desc, H),'
+        " offsetof(vidattn_rope3d_desc, d_t), offsetof(vidattn_rope3d_desc, d_w), offsetof(vidattn_rope3d_desc, theta));\n"
+        '  printf("%zu %zu %zu %zu %zu\\n", sizeof(vidattn_window_desc), offsetof(vidattn_window_desc, W),'
+        " offsetof(vidattn_window_desc, r_f), offsetof(vidattn_window_desc, r_w), offsetof(vidattn_window_desc, layout));\n"
+        '  printf("%d %d %d %d\\n", VIDATTN_WINDOW_AUTO, VIDATTN_WINDOW_ROWS, VIDATTN_WINDOW_PATCHES, VIDATTN_ABI_VERSION);\n'
+        "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc, str(src), "-o", str(exe)],
+                   check=True, capture_output=True, text=True)
+    rope, win, consts = (list(map(int, line.split())) for line in
+                         subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines())
+    R, W = va.Rope3dDesc, va.WindowDesc
+    assert rope == [ctypes.sizeof(R), R.H.offset, R.d_t.offset, R.d_w.offset, R.theta.offset]
+    assert win == [ctypes.sizeof(W), W.W.offset, W.r_f.offset, W.r_w.offset, W.layout.offset]
+    assert consts == [va.WINDOW_AUTO, va.WINDOW_ROWS, va.WINDOW_PATCHES, va.ABI_VERSION]
