@@ -498,3 +498,17 @@ def test_window_large(va, layout):
                           layout=layout)
     _log(f"  {st}")
     assert _within(st), st
+
+
+def test_window_patches_d64_ragged_grid(va):
+    """The patch layout at d = 64 on a grid whose patches are ragged in both
+    axes (44 = 2*16 + 12 rows, 70 = 4*16 + 6 columns), 2 x 3 heads, radius
+    (1, 5, 9); 256 sampled rows of two slices."""
+    wl = wlmod.custom(2, 3, (6, 44, 70), 64, (16, 24, 24), seed_id=705)
+    host = parity.host_inputs(wl)
+    rows = wlmod.sample_rows(wl, 0, 0)
+    _log(f"window {wl.name} radius=(1, 5, 9) layout=patches")
+    _, st = _check_window(va, wl, host, (1, 5, 9), rows=rows, slices=[(0, 0), (wl.B - 1, wl.heads - 1)],
+                          layout="patches")
+    _log(f"  {st}")
+    assert _within(st), st
