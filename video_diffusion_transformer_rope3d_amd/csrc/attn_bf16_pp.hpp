@@ -8,10 +8,14 @@
 // every LDS read is one conflict-free ds_read_b128 per lane).
 //
 // Per wave and tile j there are two phases:
-//   GEMM_j     O^T += V_{j-1}^T P_{j-1}^T   (16 x v_mfma_f32_32x32x16_bf16)
-//              S'^T = K_j Q'^T - m          (16 x v_mfma_f32_32x32x16_f16)
+//   GEMM_j     O^T += V_{j-1}^T P_{j-1}^T   (32 x v_mfma_f32_16x16x32_bf16)
+//              S'^T = K_j Q'^T - m          (32 x v_mfma_f32_16x16x32_f16)
 //   SOFTMAX_j  P_j = exp2(S'_j) -> bf16, rare exact rescale, row sums
 //              (group B adds its row sums in its next GEMM phase)
+// The 16x16 products take each LDS operand block twice, once per 16-query
+// half of the wave, so a wave reads the same LDS bytes per tile as one
+// 32x32 product would; measured on this chip, the 16x16x32 instructions
+// draw less power per FLOP on real data, and the kernel is power-limited.
 // Waves 0-3 (group A) and 4-7 (group B) sit one per SIMD each (the hardware
 // places wave w and w+4 of a workgroup on the same SIMD). One barrier opens
 // each tile period; in it group A runs GEMM then SOFTMAX and group B runs
@@ -26,14 +30,20 @@
 // tile j+NS-1, at the start of their softmax phase (the sparse variants
 // split them with group B, which issues its share at the period start).
 //
-// Numerics: the transposed products put all
-// scores and outputs of query q in lanes q and q+32, and m + 20 (m the
-// running maximum, in log2 units) enters as the accumulator input of the
-// first score MFMA, so P = exp2(s - m - 20) is at most 2^-20 at the maximum.
-// m moves only when some probability of a tile reaches 2 (a score more than
-// 21 above m, or a non-finite one), which one bit of the OR of the bf16
-// probabilities shows; then the tile is redone against the exact maximum and
-// O, l are scaled. The common factor 2^-20 cancels in O / l.
+// Lanes: lane i + 16r (i < 16, r < 4) holds, for each half h < 2 of the
+// wave, query 16h + i: its scores for keys 32s + 8r .. 32s + 8r + 7 of each
+// 32-key step s (score_key order), its outputs for head dims 16db + 4r ..
+// 16db + 4r + 3, and head dims 32s + 8r .. + 7 of its rotated query. A
+// query's scores and outputs are thus spread over the four lanes i, i + 16,
+// i + 32, i + 48.
+//
+// Numerics: m + 20 (m the running maximum, in log2 units) enters as the
+// accumulator input of the first score MFMA, so P = exp2(s - m - 20) is at
+// most 2^-20 at the maximum. m moves only when some probability of a tile
+// reaches 2 (a score more than 21 above m, or a non-finite one), which one
+// bit of the OR of the bf16 probabilities shows; then the tile is redone
+// against the exact maximum and O, l are scaled. The common factor 2^-20
+// cancels in O / l.
 //
 // Three variants share the loop. Query subset: Nq query rows (Nq may differ
 // from the Nk keys) whose rotary positions are the token indices qidx[row]
@@ -87,6 +97,8 @@ struct WindowParams {
 // (int)fma(k, inv, inv / 2) = k / n for 0 <= k < 2^22 and inv = 1/n in fp32.
 __device__ __forceinline__ int div_small(int k, float inv) { return (int)__builtin_fmaf((float)k, inv, 0.5f * inv); }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 template <int D, int NS, bool SPARSE, int WIN = kWinNone>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ ws, uint16_t* __restrict__ O, int N, int nkt, int Nq,
@@ -97,9 +109,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   constexpr int NW = 8;
   constexpr int KT = 64;
   constexpr int BR = NW * 32;
-  constexpr int KSTEPS = D / 16;  // 16-wide head-dim steps of the score product
-  constexpr int DB = D / 32;      // 32-wide head-dim blocks of the output
-  constexpr int MS = KT / 16;     // 16-key steps of the P.V product
+  constexpr int KS = D / 32;    // 32-wide head-dim steps of the score product
+  constexpr int DB = D / 16;    // 16-wide head-dim blocks of the output
+  constexpr int NKB = KT / 16;  // 16-key blocks of a tile's scores
+  constexpr int MS = KT / 32;   // 32-key steps of the P.V product
   constexpr int TILE = KT * D * 2;  // bytes of one K tile (and of one V tile)
   constexpr int STAGE = 2 * TILE;
   // Dense: the waves of group A refill the ring. Sparse variants, whose
@@ -120,7 +133,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = wave >> 2;  // 0: GEMM then softmax in each period, 1: the reverse
-  const int g = lane >> 5, qi = lane & 31;
+  const int qi = lane & 15, r4 = lane >> 4;
 
   // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
   // contiguous range of (bh, query tile) so the workgroups resident on one
@@ -151,36 +164,41 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       return j;
     }
   };
-  // This lane's query row: its row index in Q and O, and whether it exists
-  // (in the patch layout, rows past the grid's edge do not; their grid
-  // position (pf, py0 + r/16, px0 + r%16) still serves the rotation).
-  int qtok;
-  bool qvalid;
+  // This lane's two query rows (h = 0, 1: row wave*32 + 16h + qi of the
+  // block): their row indices in Q and O, and whether they exist (in the
+  // patch layout, rows past the grid's edge do not; their grid position
+  // (pf, py0 + 2 wave + h, px0 + qi) still serves the rotation).
+  int qtok[2];
+  bool qvalid[2];
   int pf = 0, py0 = 0, px0 = 0;  // the patch's frame, first row and first column
-  {
-    const int r = wave * 32 + qi;
+  if constexpr (WIN == kWinPatch) {
+    const int b2 = div_small(qt, wp.invpxn), px = qt - b2 * wp.pxn;
+    pf = div_small(b2, wp.invpyn);
+    const int py = b2 - pf * wp.pyn;
+    py0 = 16 * py;
+    px0 = 16 * px;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = wave * 32 + 16 * h + qi;
     if constexpr (WIN == kWinPatch) {
-      const int b2 = div_small(qt, wp.invpxn), px = qt - b2 * wp.pxn;
-      pf = div_small(b2, wp.invpyn);
-      const int py = b2 - pf * wp.pyn;
-      py0 = 16 * py;
-      px0 = 16 * px;
       const int y = py0 + (r >> 4), x = px0 + (r & 15);
-      qvalid = y < wp.H && x < wp.W;
-      qtok = qvalid ? (pf * wp.H + y) * wp.W + x : 0;
+      qvalid[h] = y < wp.H && x < wp.W;
+      qtok[h] = qvalid[h] ? (pf * wp.H + y) * wp.W + x : 0;
     } else {
-      qtok = qt * BR + r;
-      qvalid = qtok < Nq;
-      if (!qvalid) qtok = 0;
+      qtok[h] = qt * BR + r;
+      qvalid[h] = qtok[h] < Nq;
+      if (!qvalid[h]) qtok[h] = 0;
     }
   }
   if (SPARSE && nt == 0) {  // no key visited: O = 0 for the block's rows
-    if (qvalid) {
-      uint16_t* orow = O + ((int64_t)bh * Nq + qtok) * D;
 #pragma unroll
-      for (int c = 0; c < D / 8; c += 2)
-        *reinterpret_cast<u32x4*>(orow + 8 * (c + g)) = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int h = 0; h < 2; ++h)
+      if (qvalid[h]) {
+        uint16_t* orow = O + ((int64_t)bh * Nq + qtok[h]) * D;
+#pragma unroll
+        for (int c = 0; c < KS; ++c) *reinterpret_cast<u32x4*>(orow + 32 * c + 8 * r4) = u32x4{0u, 0u, 0u, 0u};
+      }
     return;
   }
 
@@ -205,33 +223,39 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   };
   // ---- queries: rotate, pre-scale by scale*log2(e), round to fp16 (B operand).
   // Their loads are issued before any tile load, so waiting for tile 0 covers them.
-  half8 qreg[KSTEPS];
+  half8 qreg[KS][2];
   {
-    const uint16_t* qrow = Q + ((int64_t)bh * Nq + qtok) * D;
-    u32x4 raw[KSTEPS];
+    u32x4 raw[2][KS];
+    int pos[2];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * g);
-    // rotary position of this row: its token index in the grid
-    int pos = qtok;
-    if (qidx) {
-      const int t = qidx[pos];
-      pos = t < 0 ? 0 : (t < N ? t : N - 1);
+    for (int h = 0; h < 2; ++h) {
+      const uint16_t* qrow = Q + ((int64_t)bh * Nq + qtok[h]) * D;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) raw[h][s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * r4);
+      // rotary position of this row: its token index in the grid
+      pos[h] = qtok[h];
+      if (qidx) {
+        const int t = qidx[pos[h]];
+        pos[h] = t < 0 ? 0 : (t < N ? t : N - 1);
+      }
     }
     if (kFillB || group == 0)
       for (int j = 0; j < NS - 1; ++j)
         if (j <= nt) issue(j, tile_at(j), tile_at(j - 1));
-    // grid coordinates of the row, once
+    // grid coordinates of the rows, once
     const int hw = rp.H * rp.W;
-    int cf, cy, cx;
-    if constexpr (WIN == kWinPatch) {
-      const int r = wave * 32 + qi;
-      cf = pf;
-      cy = py0 + (r >> 4);
-      cx = px0 + (r & 15);
-    } else {
-      cf = rp.enabled ? pos / hw : 0;
-      cy = rp.enabled ? (pos - cf * hw) / rp.W : 0;
-      cx = pos - cf * hw - cy * rp.W;
+    int cf[2], cy[2], cx[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (WIN == kWinPatch) {
+        cf[h] = pf;
+        cy[h] = py0 + 2 * wave + h;
+        cx[h] = px0 + qi;
+      } else {
+        cf[h] = rp.enabled ? pos[h] / hw : 0;
+        cy[h] = rp.enabled ? (pos[h] - cf[h] * hw) / rp.W : 0;
+        cx[h] = pos[h] - cf[h] * hw - cy[h] * rp.W;
+      }
     }
     // Window variants: the cos/sin of every (axis position, pair) the
     // workgroup's rows can use, once per workgroup, in the ring stage the
@@ -274,166 +298,190 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       lds_barrier();
     }
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      float x[8];
-      unpack_bf16x8(raw[s], x);
+    for (int s = 0; s < KS; ++s) {
+      float x[2][8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) unpack_bf16x8(raw[h][s], x[h]);
       if (rp.enabled) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // pair 8s + 4g + j: both candidates (g = 0, 1) are wave-uniform
-          // kernel arguments, read once into scalar registers
-          const int p0 = 8 * s + j, p1 = p0 + 4;
-          float c, sn;
+          // pair 16s + 4r + j: its four candidates (r = 0..3) are
+          // wave-uniform kernel arguments, read once into scalar registers
+          const int p = 16 * s + 4 * r4 + j;
           if (table) {
-            const int p = g ? p1 : p0;
-            const int e = p < rp.pair_t ? (cf - f0) * npt + p
-                                        : (p < rp.pair_th ? base_h + (cy - y0) * nph + (p - rp.pair_t)
-                                                          : base_w + (cx - x0) * npw + (p - rp.pair_th));
-            const float2 cs = tbl[e];
-            c = cs.x;
-            sn = cs.y;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int e = p < rp.pair_t ? (cf[h] - f0) * npt + p
+                                          : (p < rp.pair_th ? base_h + (cy[h] - y0) * nph + (p - rp.pair_t)
+                                                            : base_w + (cx[h] - x0) * npw + (p - rp.pair_th));
+              const float2 cs = tbl[e];
+              rotate_pair(x[h][2 * j], x[h][2 * j + 1], cs.x, cs.y);
+            }
           } else {
-            const double w0 = uniform_f64(rp.omega[p0]), w1 = uniform_f64(rp.omega[p1]);
-            const int a0 = p0 < rp.pair_t ? cf : (p0 < rp.pair_th ? cy : cx);
-            const int a1 = p1 < rp.pair_t ? cf : (p1 < rp.pair_th ? cy : cx);
-            rope_angle_cos_sin(g ? a1 : a0, g ? w1 : w0, c, sn);
+            double wr[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) wr[rr] = uniform_f64(rp.omega[16 * s + 4 * rr + j]);
+            const double w = r4 == 0 ? wr[0] : (r4 == 1 ? wr[1] : (r4 == 2 ? wr[2] : wr[3]));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int a = p < rp.pair_t ? cf[h] : (p < rp.pair_th ? cy[h] : cx[h]);
+              float c, sn;
+              rope_angle_cos_sin(a, w, c, sn);
+              rotate_pair(x[h][2 * j], x[h][2 * j + 1], c, sn);
+            }
           }
-          rotate_pair(x[2 * j], x[2 * j + 1], c, sn);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qreg[s][j] = (_Float16)(qvalid ? x[j] * qscale : 0.f);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qreg[s][h][j] = (_Float16)(qvalid[h] ? x[h][j] * qscale : 0.f);
     }
   }
 
-  f32x16 oacc[DB];
-  f32x16 negm;  // -m broadcast: accumulator input of the first score MFMA
-  f32x16 sacc[2];
-  bf16x8 pk[MS];
-  float m = 0.f, l = 0.f;
-  bool m_valid = false;  // this row's m comes from a visible key
+  f32x4 oacc[DB][2];
+  f32x4 negm[2];  // -m broadcast: accumulator input of the first score MFMA
+  f32x4 sacc[NKB][2];
+  bf16x8 pk[MS][2];
+  float m[2] = {0.f, 0.f}, l[2] = {0.f, 0.f};
+  bool m_valid[2] = {false, false};  // the row's m comes from a visible key
   // window bits of the tile whose scores the last GEMM phase produced (the
-  // softmax phase that follows reads them; in the patch layout ~0 or 0,
-  // whether the query sees any key of the tile); all keys count as visible
-  // outside the window variants
+  // softmax phase that follows reads them): bit 16h + 4kb + i for score i of
+  // key block kb of half h; in the patch layout all 16 bits of a half are
+  // equal (whether its query sees any key of the tile); all keys count as
+  // visible outside the window variants
   unsigned wvis = ~0u;
-  // Window of this lane's query (window variant): a key at (f, y, x) is
+  // Window of this lane's queries (window variant): a key at (f, y, x) is
   // visible when f - flo, y - ylo and x - clo, as unsigned, are at most
   // 2 r_f, 2 r_h and 2 r_w. For the fast test, a run of 8 keys starting at
   // column c0 of row r0 sees columns [clo, cend) of row r0 and, after the
   // row wrap, [wlo, wend) counted from the run's start as W - c0 + column.
-  // The patch layout tests rows and columns on their own: this lane's query
-  // sees grid rows [ylo, yend) and columns [clo, cend).
-  int flo = 0, ylo = 0, clo = 0, cend = 0, wlo = 0, wend = 0, yend = 0;
+  // The patch layout tests rows and columns on their own: the query sees
+  // grid rows [ylo, yend) and columns [clo, cend).
+  int flo[2] = {0, 0}, ylo[2] = {0, 0}, clo[2] = {0, 0}, cend[2] = {0, 0};
+  int wlo[2] = {0, 0}, wend[2] = {0, 0}, yend[2] = {0, 0};
   if constexpr (WIN != kWinNone) {
-    int qf, qy, qx;
-    if constexpr (WIN == kWinPatch) {
-      const int r = wave * 32 + qi;
-      qf = pf;
-      qy = py0 + (r >> 4);
-      qx = px0 + (r & 15);
-    } else {
-      const int t = qtok;
-      const int hw = wp.H * wp.W;
-      qf = t / hw;
-      qy = (t - qf * hw) / wp.W;
-      qx = t - qf * hw - qy * wp.W;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int qf, qy, qx;
+      if constexpr (WIN == kWinPatch) {
+        qf = pf;
+        qy = py0 + 2 * wave + h;
+        qx = px0 + qi;
+      } else {
+        const int t = qtok[h];
+        const int hw = wp.H * wp.W;
+        qf = t / hw;
+        qy = (t - qf * hw) / wp.W;
+        qx = t - qf * hw - qy * wp.W;
+      }
+      flo[h] = qf - wp.rf;
+      ylo[h] = qy - wp.rh;
+      clo[h] = qx - wp.rw;
+      const int chi = qx + wp.rw < wp.W - 1 ? qx + wp.rw : wp.W - 1;
+      cend[h] = chi + 1;
+      wlo[h] = wp.W + (clo[h] > 0 ? clo[h] : 0);
+      wend[h] = wp.W + chi + 1;
+      yend[h] = (qy + wp.rh < wp.H - 1 ? qy + wp.rh : wp.H - 1) + 1;
     }
-    flo = qf - wp.rf;
-    ylo = qy - wp.rh;
-    clo = qx - wp.rw;
-    const int chi = qx + wp.rw < wp.W - 1 ? qx + wp.rw : wp.W - 1;
-    cend = chi + 1;
-    wlo = wp.W + (clo > 0 ? clo : 0);
-    wend = wp.W + chi + 1;
-    yend = (qy + wp.rh < wp.H - 1 ? qy + wp.rh : wp.H - 1) + 1;
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) negm[i] = -kBias;
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) negm[h][i] = -kBias;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[db][h][i] = 0.f;
 
-  // P = exp2(S') as bf16 B operands. Score register i of key block kb is key
-  // 32kb + 16(i/8) + 8g + i%8, so pk[ms] holds keys 16ms + 8g .. +7. Returns
-  // the OR of the probabilities' bits (a balanced tree: it is on the path to
-  // the exact-step test).
+  // P = exp2(S') as bf16 B operands: pk[s][h] holds keys 32s + 8r .. + 7 of
+  // half h (score blocks 2s and 2s + 1). Returns the OR of the
+  // probabilities' bits (a balanced tree: it is on the path to the
+  // exact-step test).
   auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int s = 0; s < MS; ++s)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         bf16x8 p;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * h + j]);
-        pk[2 * kb + h] = p;
+        for (int e = 0; e < 8; ++e) p[e] = (__bf16)__builtin_amdgcn_exp2f(sacc[2 * s + (e >> 2)][h][e & 3]);
+        pk[s][h] = p;
       }
-    uint32_t w[4 * MS];
+    uint32_t w[16];
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      const bf16x8 pv = pk[ms];
-      const u32x4 x = __builtin_bit_cast(u32x4, pv);
+    for (int s = 0; s < MS; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[4 * ms + e] = x[e];
-    }
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 pv = pk[s][h];
+        const u32x4 x = __builtin_bit_cast(u32x4, pv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[8 * s + 4 * h + e] = x[e];
+      }
     // (the empty asm statements keep the compiler from re-associating the
     // tree into one serial chain)
     uint32_t a = w[0] | w[1] | w[2], b = w[3] | w[4] | w[5], c = w[6] | w[7] | w[8];
     uint32_t d = w[9] | w[10] | w[11], e = w[12] | w[13] | w[14];
     asm("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e));
-    uint32_t f = a | b | c, h = d | e | w[15];
-    asm("" : "+v"(f), "+v"(h));
-    return f | h;
+    uint32_t f = a | b | c, g = d | e | w[15];
+    asm("" : "+v"(f), "+v"(g));
+    return f | g;
   };
-  // The lane's partial row sum of the rounded probabilities.
+  // Adds the lane's partial row sums of the rounded probabilities to l.
   auto rowsum = [&]() __attribute__((always_inline)) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    float part[MS];
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      float acc = 0.f;
+    for (int h = 0; h < 2; ++h) {
+      float part[MS];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 pp = {pk[ms][2 * j], pk[ms][2 * j + 1]};
-        acc = __builtin_amdgcn_fdot2_f32_bf16(pp, one, acc, false);
+      for (int s = 0; s < MS; ++s) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pp = {pk[s][h][2 * j], pk[s][h][2 * j + 1]};
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pp, one, acc, false);
+        }
+        part[s] = acc;
       }
-      part[ms] = acc;
+      l[h] += part[0] + part[1];
     }
-    return (part[0] + part[1]) + (part[2] + part[3]);
   };
   // The exact step's rescale: the tile's exact maximum (relative to the
   // current m) becomes part of m; a row that has seen no visible key yet
   // takes the tile's maximum as its m (and keeps m = 0 if the tile shows it
-  // none). O is scaled, the scores are moved to the new m; returns alpha,
-  // the factor l must be scaled by.
+  // none). O and l are scaled, the scores are moved to the new m.
   auto rescale_to_tile_max = [&]() __attribute__((always_inline)) {
-    float mx = sacc[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int h = 0; h < 2; ++h) {
+      float mx = sacc[0][h][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = xor32_max(mx) + kBias;
-    // (in the patch layout a hidden key's score is finite, and wvis, the
-    // same in both halves of the wave, decides; elsewhere wvis covers only
-    // this lane's half of the tile)
-    const bool seen = WIN == kWinPatch ? wvis != 0u : mx > -INFINITY;
-    const float delta = !m_valid ? (seen ? mx : 0.f) : fmaxf(mx, 0.f);
-    const float alpha = !m_valid ? 1.f : __builtin_amdgcn_exp2f(-delta);
-    m_valid = m_valid || seen;
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][h][i]);
+      mx = xor32_max(xor16_max(mx)) + kBias;
+      // (in the patch layout a hidden key's score is finite, and wvis, the
+      // same in the four lanes of a row, decides; elsewhere the row maximum
+      // does)
+      const bool seen = WIN == kWinPatch ? ((wvis >> (16 * h)) & 0xFFFFu) != 0u : mx > -INFINITY;
+      const float delta = !m_valid[h] ? (seen ? mx : 0.f) : fmaxf(mx, 0.f);
+      const float alpha = !m_valid[h] ? 1.f : __builtin_amdgcn_exp2f(-delta);
+      m_valid[h] = m_valid[h] || seen;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    m += delta;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) negm[i] = -(m + kBias);
+        for (int i = 0; i < 4; ++i) oacc[db][h][i] *= alpha;
+      l[h] *= alpha;
+      m[h] += delta;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 4; ++i) negm[h][i] = -(m[h] + kBias);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] -= delta;
-    return alpha;
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[kb][h][i] -= delta;
+    }
   };
 
   constexpr int kWaitNewer = STAGE_LOADS * (NS - 2);
@@ -453,11 +501,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     lds_barrier();
   };
 
-  // Window variant: bit 8(2kb + h) + e of window_vis(t) is set when this
-  // lane's key 32kb + 16h + 8g + e of workspace tile t lies inside its query's box.
-  // It depends on the tile and the query only, so the GEMM phase folds it
-  // into the accumulator input of the first score MFMA (-m, or -inf for a
-  // key outside the box) while the matrix core runs the P.V products.
+  // Window variant: bit 16h + 8s + e of window_vis(t) is set when key
+  // 32s + 8r + e of workspace tile t (this lane's run e < 8 of step s) lies
+  // inside the box of its query of half h. It depends on the tile and the
+  // queries only, so the GEMM phase folds it into the accumulator input of
+  // the first score MFMA (-m, or -inf for a key outside the box) while the
+  // matrix core runs the P.V products.
   auto window_vis = [&](int tile) __attribute__((always_inline)) {
     unsigned vis = 0;
     if constexpr (WIN == kWinRows) {
@@ -479,13 +528,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         const bool wrap = yb == wp.H - 1;
         const int y1 = wrap ? 0 : yb + 1;
         const int f1 = fb + (wrap ? 1 : 0);
-        const bool row0 = ((unsigned)(fb - flo) <= fspan) & ((unsigned)(yb - ylo) <= yspan);
-        const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
-        const uint64_t m = (row0 ? bits64(clo - cb, cend - cb) : (uint64_t)0) |
-                           (row1 ? bits64(wlo - cb, wend - cb) : (uint64_t)0);
-        // this lane's keys are the runs at tile offsets 16u + 8g (u = 2kb + h):
-        // bytes g, 2 + g, 4 + g, 6 + g of m
-        vis = __builtin_amdgcn_perm((unsigned)(m >> 32), (unsigned)m, g ? 0x07050301u : 0x06040200u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool row0 = ((unsigned)(fb - flo[h]) <= fspan) & ((unsigned)(yb - ylo[h]) <= yspan);
+          const bool row1 = ((unsigned)(f1 - flo[h]) <= fspan) & ((unsigned)(y1 - ylo[h]) <= yspan);
+          const uint64_t mm = (row0 ? bits64(clo[h] - cb, cend[h] - cb) : (uint64_t)0) |
+                              (row1 ? bits64(wlo[h] - cb, wend[h] - cb) : (uint64_t)0);
+          // this lane's keys are the runs at tile offsets 8r and 32 + 8r:
+          // bytes r and 4 + r of mm
+          const unsigned lo = (unsigned)mm, hi = (unsigned)(mm >> 32);
+          const unsigned run = ((lo >> (8 * r4)) & 0xFFu) | (((hi >> (8 * r4)) & 0xFFu) << 8);
+          vis |= run << (16 * h);
+        }
       } else if (wp.mode == 1) {
         // W >= 8: a run covers at most rows r0 and r0 + 1. Its visible keys
         // form one bit range per row; the row test gates each range.
@@ -495,8 +549,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           return (1u << hi) - (1u << lo);
         };
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k0 = base + 16 * u + 8 * g;
+        for (int s = 0; s < MS; ++s) {
+          const int k0 = base + 32 * s + 8 * r4;
           const int r0 = (int)__builtin_fmaf((float)k0, wp.invW, hinvW);
           const int c0 = k0 - __mul24(r0, wp.W);
           const int f0 = (int)__builtin_fmaf((float)r0, wp.invH, hinvH);
@@ -504,26 +558,33 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           const bool wrap = y0 == wp.H - 1;
           const int y1 = wrap ? 0 : y0 + 1;
           const int f1 = f0 + (wrap ? 1 : 0);
-          const bool row0 = ((unsigned)(f0 - flo) <= fspan) & ((unsigned)(y0 - ylo) <= yspan);
-          const bool row1 = ((unsigned)(f1 - flo) <= fspan) & ((unsigned)(y1 - ylo) <= yspan);
-          const unsigned rv = (row0 ? bits(clo - c0, cend - c0) : 0u) | (row1 ? bits(wlo - c0, wend - c0) : 0u);
-          vis |= rv << (8 * u);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const bool row0 = ((unsigned)(f0 - flo[h]) <= fspan) & ((unsigned)(y0 - ylo[h]) <= yspan);
+            const bool row1 = ((unsigned)(f1 - flo[h]) <= fspan) & ((unsigned)(y1 - ylo[h]) <= yspan);
+            const unsigned rv =
+                (row0 ? bits(clo[h] - c0, cend[h] - c0) : 0u) | (row1 ? bits(wlo[h] - c0, wend[h] - c0) : 0u);
+            vis |= rv << (16 * h + 8 * s);
+          }
         }
       } else {
         // general grid: decode each run's first key, then step the column
         // index with carries into row and frame
         const int hw = wp.H * wp.W;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k0 = base + 16 * u + 8 * g;
+        for (int s = 0; s < MS; ++s) {
+          const int k0 = base + 32 * s + 8 * r4;
           int f = k0 / hw;
           int y = (k0 - f * hw) / wp.W;
           int x = k0 - f * hw - y * wp.W;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const bool in = ((unsigned)(f - flo) <= fspan) & ((unsigned)(y - ylo) <= yspan) &
-                            ((unsigned)(x - clo) <= xspan);
-            vis |= (in ? 1u : 0u) << (8 * u + e);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const bool in = ((unsigned)(f - flo[h]) <= fspan) & ((unsigned)(y - ylo[h]) <= yspan) &
+                              ((unsigned)(x - clo[h]) <= xspan);
+              vis |= (in ? 1u : 0u) << (16 * h + 8 * s + e);
+            }
             const bool cx = x == wp.W - 1;
             x = cx ? 0 : x + 1;
             const bool cy = cx & (y == wp.H - 1);
@@ -537,28 +598,32 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   };
 
   // Patch layout: the box test runs on the matrix core. Key kk of a tile
-  // lies in tile row kk/8 and column kk%8, so an extra score MFMA per key
-  // block, with a one-hot A operand (the key's row among k = 0..7, its
-  // column among k = 8..15) and a B operand of per-query penalties (0 for a
-  // tile row or column the query sees, -3.39e38 for one it does not), turns
-  // the accumulator input -m into exactly -m for a visible key and into at
-  // most -3.39e38 (or -inf) for a hidden one; the score products that follow
-  // (at most 2^40 in size) cannot lift it. Its products are 1 x pen or
-  // 0 x pen, never 0 x inf, so no NaN arises.
-  bf16x8 onehot[2];
+  // lies in tile row kk/8 and column kk%8, so an extra 16x16x16 MFMA per key
+  // block and query half, with a one-hot A operand (the key's row among
+  // k = 0..7, its column among k = 8..15) and a B operand of per-query
+  // penalties (0 for a tile row or column the query sees, -3.39e38 for one
+  // it does not), turns the accumulator input -m into exactly -m for a
+  // visible key and into at most -3.39e38 (or -inf) for a hidden one; the
+  // score products that follow (at most 2^40 in size) cannot lift it. Its
+  // products are 1 x pen or 0 x pen, never 0 x inf, so no NaN arises.
+  // (16x16x16 operands: lane i + 16r holds k = 4r .. 4r + 3 of row/column i.)
+  s16x4 onehot[NKB];
   if constexpr (WIN == kWinPatch) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kk = 32 * kb + rho32(qi);  // the key of A row qi in key block kb
-      const int hot = g ? (kk & 7) : (kk >> 3);
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int kk = score_key(kb, qi);  // the key of A row qi in key block kb
+      const int hot = r4 < 2 ? (kk >> 3) - 4 * r4 : (kk & 7) - 4 * (r4 - 2);
+      bf16x4 v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) onehot[kb][j] = (__bf16)(j == hot ? 1.f : 0.f);
+      for (int j = 0; j < 4; ++j) v[j] = (__bf16)(j == hot ? 1.f : 0.f);
+      onehot[kb] = __builtin_bit_cast(s16x4, v);
     }
   }
-  // The penalty operand of the tile the next score product covers (this
-  // lane's half: rows for g = 0, columns for g = 1) and whether the lane's
-  // query sees any of its keys (it becomes wvis once the scores exist).
-  bf16x8 pen_sc;
+  // The penalty operands of the tile the next score product covers (this
+  // lane's quarter: tile rows 4r .. 4r + 3 for r < 2, columns 4(r - 2) ..
+  // for r >= 2) and whether each query sees any of its keys (it becomes
+  // wvis once the scores exist).
+  s16x4 pen_sc[2];
   unsigned vis_sc = ~0u;
   // Sets pen_sc and vis_sc for tile t and returns whether any query of the
   // wave sees a key of it. A wave that sees none skips the tile's score
@@ -574,17 +639,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         const int hi = b < lo ? lo : (b > 8 ? 8 : b);
         return (1u << hi) - (1u << lo);
       };
-      const unsigned rows = bits8(ylo - 8 * ty, yend - 8 * ty);
-      const unsigned cols = bits8(clo - 8 * tx, cend - 8 * tx);
-      const bool fok = (unsigned)(tf - flo) <= 2u * wp.rf;
-      vis_sc = fok && rows != 0u && cols != 0u ? ~0u : 0u;
-      const unsigned hide = fok ? ~(g ? cols : rows) : ~0u;
-      u32x4 w;
+      const unsigned cols = bits8(clo[0] - 8 * tx, cend[0] - 8 * tx);  // (both rows share the column)
+      const bool fok = (unsigned)(tf - flo[0]) <= 2u * wp.rf;
+      unsigned vis = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)  // bf16 0xFF7F = -3.39e38 for a hidden row or column
-        w[e] = (((hide >> (2 * e)) & 1u) | (((hide >> (2 * e + 1)) & 1u) << 16)) * 0xFF7Fu;
-      pen_sc = __builtin_bit_cast(bf16x8, w);
-      return __builtin_amdgcn_ballot_w64(vis_sc != 0u) != 0;
+      for (int h = 0; h < 2; ++h) {
+        const unsigned rows = bits8(ylo[h] - 8 * ty, yend[h] - 8 * ty);
+        vis |= fok && rows != 0u && cols != 0u ? 0xFFFFu << (16 * h) : 0u;
+        const unsigned hide = (fok ? ~(r4 < 2 ? rows : cols) : ~0u) >> (4 * (r4 & 1));
+        u32x2 w;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)  // bf16 0xFF7F = -3.39e38 for a hidden row or column
+          w[e] = (((hide >> (2 * e)) & 1u) | (((hide >> (2 * e + 1)) & 1u) << 16)) * 0xFF7Fu;
+        pen_sc[h] = __builtin_bit_cast(s16x4, w);
+      }
+      vis_sc = vis;
+      return __builtin_amdgcn_ballot_w64(vis != 0u) != 0;
     } else {
       (void)tile;
       return true;
@@ -630,14 +700,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // The first operand batch of a GEMM phase with the P.V product (V blocks
   // 0 .. RB-1). Group B reads it right after the barrier, ahead of its
   // softmax, so that its GEMM phase starts without an LDS wait.
-  auto vb = [&](int i) __attribute__((always_inline)) { return (i % DB) * MS + i / DB; };
   auto first_batch = [&](int jj) __attribute__((always_inline)) {
     const uint8_t* st = stage_ptr(jj);
     Batch b;
     b.st = st;
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
-      b.v[r] = *reinterpret_cast<const u32x4*>(st + TILE + vb(r) * 1024);
+    for (int r = 0; r < RB; ++r) b.v[r] = *reinterpret_cast<const u32x4*>(st + TILE + r * 1024);
     __builtin_amdgcn_sched_barrier(0);  // issue the reads before what follows
     return b;
   };
@@ -646,48 +714,51 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // of the MFMAs). PRE: the first operand batch was read ahead (pre).
   auto gemm = [&](auto PV, auto SC, int jj, auto SUM, auto PRE, const Batch& pre) __attribute__((always_inline)) {
     const uint8_t* st = decltype(PRE)::value ? pre.st : stage_ptr(jj);
-    constexpr int NV = decltype(PV)::value ? DB * MS : 0;  // V^T operand blocks
-    constexpr int NK = decltype(SC)::value ? 2 * KSTEPS : 0;  // K operand blocks
+    constexpr int NV = decltype(PV)::value ? DB * MS : 0;   // V^T operand blocks
+    constexpr int NK = decltype(SC)::value ? NKB * KS : 0;  // K operand blocks
     constexpr int NOP = NV + NK;
     static_assert(NOP % RB == 0, "operand batches");
     constexpr int NB = NOP / RB;
     // scheduling groups that keep the batch structure of batches b0 .. b1:
-    // the reads of batch b + 1, then the MFMAs of batch b
+    // the reads of batch b + 1, then the MFMAs of batch b (two per operand)
     // (the patch layout's box MFMAs join the batch of the first K operand)
     constexpr bool kBox = WIN == kWinPatch && decltype(SC)::value;
     auto groups = [&](int b0, int b1) __attribute__((always_inline)) {
       for (int b = b0; b <= b1; ++b) {
         if (b + 1 < NB) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
         if (kBox && b == NV / RB)
-          __builtin_amdgcn_sched_group_barrier(0x008, RB + 2, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB + 2 * NKB, 0);  // MFMA
         else
-          __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
       }
     };
-    // Operand i < NV is V block vb(i) = (db, ms), else K block kbs(i - NV) =
-    // (kb, s). Consecutive MFMAs share their register operand (P block ms
-    // for DB products, Q step s for the two key blocks) and write different
-    // accumulators; each accumulator still sums in the same order.
-    auto kbs = [&](int i) __attribute__((always_inline)) { return (i % 2) * KSTEPS + i / 2; };
+    // Operand i < NV is V block i = (s, db) (db fastest, workspace order),
+    // else K block kbs(i - NV) = (kb, s) (kb fastest). Each operand feeds
+    // the two query halves; consecutive V blocks share their P operand.
+    // Every accumulator still sums in head-dim (K) or key (V) order.
+    auto kbs = [&](int i) __attribute__((always_inline)) { return (i % NKB) * KS + i / NKB; };
     auto addr = [&](int i) __attribute__((always_inline)) {
-      return st + (i < NV ? TILE + vb(i) * 1024 : kbs(i - NV) * 1024);
+      return st + (i < NV ? TILE + i * 1024 : kbs(i - NV) * 1024);
     };
-    // accumulator input of the first score MFMA per key block: -m, or -inf
-    // for a key outside the window (sign-extended bit, then a bit select)
-    f32x16 cneg[2];
+    // accumulator input of the first score MFMA per key block and half: -m,
+    // or -inf for a key outside the window (sign-extended bit, then a bit
+    // select)
+    f32x4 cneg[NKB][2];
     if constexpr (kBox) wvis = vis_sc;
     if constexpr (WIN == kWinRows && decltype(SC)::value) {
       const unsigned vis = window_vis(tw[1]);
       wvis = vis;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const unsigned keep = (unsigned)((int)(vis << (31 - (16 * kb + i))) >> 31);
-          const float mv = negm[i];  // (bit-casting the element expression itself reads element 0)
-          const unsigned mb = __builtin_bit_cast(unsigned, mv);
-          cneg[kb][i] = __builtin_bit_cast(float, (mb & keep) | (0xff800000u & ~keep));
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const unsigned keep = (unsigned)((int)(vis << (31 - (16 * h + 4 * kb + i))) >> 31);
+            const float mv = negm[h][i];  // (bit-casting the element expression itself reads element 0)
+            const unsigned mb = __builtin_bit_cast(unsigned, mv);
+            cneg[kb][h][i] = __builtin_bit_cast(float, (mb & keep) | (0xff800000u & ~keep));
+          }
     }
     u32x4 buf[2][RB];
 #pragma unroll
@@ -703,26 +774,34 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         const int i = b * RB + r;
         const u32x4 a = buf[b & 1][r];
         if (i < NV) {
-          const int db = vb(i) / MS, ms = vb(i) % MS;
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pk[ms], oacc[db], 0, 0, 0);
+          const int db = i % DB, s = i / DB;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            oacc[db][h] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pk[s][h], oacc[db][h], 0, 0, 0);
         } else {
-          const int kb = kbs(i - NV) / KSTEPS, s = kbs(i - NV) % KSTEPS;
+          const int kb = (i - NV) % NKB, s = (i - NV) / NKB;
           if constexpr (kBox) {
             if (i == NV) {
 #pragma unroll
-              for (int k2 = 0; k2 < 2; ++k2)
-                sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(onehot[k2], pen_sc, negm, 0, 0, 0);
+              for (int k2 = 0; k2 < NKB; ++k2)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                  sacc[k2][h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(onehot[k2], pen_sc[h], negm[h], 0, 0, 0);
             }
           }
-          const f32x16 c0 = WIN == kWinPatch ? sacc[kb] : (WIN == kWinRows ? cneg[kb] : negm);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), qreg[s],
-                                                            s == 0 ? c0 : sacc[kb], 0, 0, 0);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 c0 = WIN == kWinPatch ? sacc[kb][h] : (WIN == kWinRows ? cneg[kb][h] : negm[h]);
+            sacc[kb][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), qreg[s][h],
+                                                                 s == 0 ? c0 : sacc[kb][h], 0, 0, 0);
+          }
         }
       }
     }
-    if constexpr (decltype(SUM)::value) l += rowsum();
+    if constexpr (decltype(SUM)::value) rowsum();
     // keep the batch structure: the first RB reads up front (unless read
-    // ahead), then per batch the next RB reads and this batch's RB MFMAs
+    // ahead), then per batch the next RB reads and this batch's MFMAs
     if constexpr (!decltype(PRE)::value) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);
     groups(0, NB - 1);
   };
@@ -731,11 +810,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   auto tail_mask = [&](int t) __attribute__((always_inline)) {
     if (tail < KT && t == nkt - 1) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
-          if (key >= tail) sacc[kb][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int key = score_key(kb, 4 * r4 + i);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (key >= tail) sacc[kb][h][i] = -INFINITY;
         }
     }
   };
@@ -747,11 +828,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     // the exact step: for a row's first tile with a visible key (a row with
     // no visible key in this tile keeps m unset), and when a score lies more
     // than kBias + 1 above m
-    if (__builtin_amdgcn_ballot_w64((!m_valid && wvis != 0u) || big) != 0) {
-      l *= rescale_to_tile_max();
+    const bool first = (!m_valid[0] && (wvis & 0xFFFFu) != 0u) || (!m_valid[1] && (wvis >> 16) != 0u);
+    if (__builtin_amdgcn_ballot_w64(first || big) != 0) {
+      rescale_to_tile_max();
       probs();
     }
-    if constexpr (decltype(SUM)::value) l += rowsum();
+    if constexpr (decltype(SUM)::value) rowsum();
   };
   using T = std::true_type;
   using F = std::false_type;
@@ -784,7 +866,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       softmax(t, SUM);
     } else {
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms) pk[ms] = bf16x8{};
+      for (int s = 0; s < MS; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pk[s][h] = bf16x8{};
     }
   };
   // before a GEMM phase that no barrier precedes: no list read in flight
@@ -894,19 +978,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16.
-  // Output register i of lane (q, g) in head-dim block db is d = 32db + 8(i/4) + 4g + i%4.
-  const float inv = 1.0f / xor32_sum(l);
-  if (qvalid) {
-    uint16_t* orow = O + ((int64_t)bh * Nq + qtok) * D;
+  // Output register i of lane (qi, r) in head-dim block db of half h is
+  // d = 16db + 4r + i of query 16h + qi.
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int h = 0; h < 2; ++h) {
+    const float inv = 1.0f / xor32_sum(xor16_sum(l[h]));
+    if (qvalid[h]) {
+      uint16_t* orow = O + ((int64_t)bh * Nq + qtok[h]) * D;
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
+      for (int db = 0; db < DB; ++db) {
         bf16x4 v;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v[jj] = (__bf16)(oacc[db][4 * ib + jj] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * ib + 4 * g) = v;
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(oacc[db][h][i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * r4) = v;
       }
+    }
   }
 }
 

@@ -95,6 +95,15 @@ __device__ __forceinline__ float xor32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// The same for lanes l and l^16 (rows of 16 lanes swapped pairwise).
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Direct global -> LDS copy of 16 bytes per lane: lane i reads base + voff
 // (base uniform, in SGPRs; voff per lane) and the data lands at LDS byte
@@ -131,10 +140,13 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Row index permutation of a 32-row MFMA operand block: swaps bits 2 and 3.
-// Loading key rho(i) into A-operand row i of the 32x32x16 score product
-// makes the 8 scores a lane holds per 16-key step belong to 8 consecutive
-// keys, so the P.V product can read V^T with one 16-byte load per lane.
-__device__ __host__ __forceinline__ int rho32(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// Key of row i (< 16) of key block kb (< 4) in a 64-key tile's score
+// product. The 16x16 accumulator gives lane i + 16r rows 4r .. 4r + 3 of a
+// block; with this order those rows of blocks 2s and 2s + 1 are the 8
+// consecutive keys 32s + 8r .. 32s + 8r + 7, which is exactly the k-slice
+// the lane supplies as B operand of the 16x16x32 P.V product.
+__device__ __host__ __forceinline__ int score_key(int kb, int i) {
+  return 32 * (kb >> 1) + 8 * (i >> 2) + 4 * (kb & 1) + (i & 3);
+}
 
 }  // namespace vidattn

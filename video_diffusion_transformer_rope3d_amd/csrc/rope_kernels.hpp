@@ -98,13 +98,14 @@ __global__ __launch_bounds__(256) void rope3d_kernel(const TIn* in, TOut* out, i
 // ---------------------------------------------------------------- bf16 attention pre-pass
 
 // Workspace tile layout (per (b, head), per tile of KT = 64 keys; the
-// K part and the V part are TILE = 64*D*2 bytes each, K first):
-//   K part: 1 KB blocks, block (kb, s) for key block kb < 2 (32 keys) and
-//           head-dim step s < D/16; lane l = i + 32g of the block holds the
-//           16 bytes K'[32kb + rho32(i)][16s + 8g .. 16s + 8g + 7] (fp16,
-//           rotated). This is the A operand of v_mfma_f32_32x32x16_f16.
-//   V part: 1 KB blocks, block (db, m) for head-dim block db < D/32 and key
-//           step m < 4 (16 keys); lane l = i + 32g holds V[16m + 8g + j][32db + i],
+// K part and the V part are TILE = 64*D*2 bytes each, K first). Lane
+// l = i + 16r (i < 16, r < 4) of a 1 KB block holds 16 bytes:
+//   K part: block kb*(D/32) + s for key block kb < 4 (16 keys) and head-dim
+//           step s < D/32; the lane holds K'[score_key(kb, i)][32s + 8r ..
+//           32s + 8r + 7] (fp16, rotated): the A operand (row i, k-slice r)
+//           of v_mfma_f32_16x16x32_f16.
+//   V part: block ks*(D/16) + db for key step ks < 2 (32 keys) and head-dim
+//           block db < D/16; the lane holds V[32ks + 8r + j][16db + i],
 //           j < 8 (bf16): the A operand of the V^T.P^T product.
 // Key slots that hold no token (past N, or outside the grid) are zero in
 // both parts.
@@ -136,7 +137,8 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
                                                       uint8_t* __restrict__ ws, int N, int nkt, int64_t nbh,
                                                       int bh_per_block, RopeParams rp, TileMap map) {
   constexpr int KT = 64;
-  constexpr int KSTEPS = D / 16;
+  constexpr int KS = D / 32;  // 32-wide head-dim steps
+  constexpr int DB = D / 16;  // 16-wide head-dim blocks
   constexpr int TILE = KT * D * 2;
   constexpr int SLOTS = TILE / 16 / 256;  // 16-byte slots per thread per part
   constexpr int VPAD = D + 8;
@@ -152,11 +154,11 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
   for (int r = 0; r < SLOTS; ++r) {
     const int slot = t + 256 * r;
     const int blk = slot >> 6, lane = slot & 63;
-    const int i = lane & 31, g = lane >> 5;
-    const int kb = blk / KSTEPS, s = blk - kb * KSTEPS;
-    const int n = map.token<PATCH>(tile, 32 * kb + rho32(i), N);
+    const int i = lane & 15, rr = lane >> 4;
+    const int kb = blk / KS, s = blk - kb * KS;
+    const int n = map.token<PATCH>(tile, score_key(kb, i), N);
     ksrc[r] = n;
-    kchunk[r] = 2 * s + g;
+    kchunk[r] = 4 * s + rr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       cs[r][j] = 1.f;
@@ -206,10 +208,10 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
     for (int r = 0; r < SLOTS; ++r) {
       const int slot = t + 256 * r;
       const int blk = slot >> 6, lane = slot & 63;
-      const int i = lane & 31, g = lane >> 5;
-      const int db = blk >> 2, m = blk & 3;
-      const int col = 32 * db + i;
-      const int key0 = 16 * m + 8 * g;
+      const int i = lane & 15, rr = lane >> 4;
+      const int ks = blk / DB, db = blk - ks * DB;
+      const int col = 16 * db + i;
+      const int key0 = 32 * ks + 8 * rr;
       u32x4 w;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
