@@ -7,7 +7,10 @@ way with H). The exact value k/W + 1/(2W) lies at least 1/(2W) from the next
 integer and the fp32 error of the product stays below that while k < 2^22.
 This test evaluates that expression exactly as the hardware does (the fp64
 sum k * invW + invW / 2 is exact here, so rounding it once to fp32 is the
-fused multiply-add) for every k below 2^22 and a spread of divisors."""
+fused multiply-add) for every k below 2^22 and a spread of divisors. The
+kernel writes it as trunc((k + 1/2) * invW): k + 1/2 is exact in fp32 below
+2^23 and the product rounds the same exact value once, so the two forms give
+the same bits, which the test checks as well."""
 import numpy as np
 import pytest
 
@@ -24,6 +27,14 @@ def fast_quotient(k: np.ndarray, w: int) -> np.ndarray:
     return exact.astype(np.float32).astype(np.int64)  # one rounding, then truncation
 
 
+def kernel_quotient(k: np.ndarray, w: int) -> np.ndarray:
+    """The form the kernel evaluates: fp32 k + 0.5 (exact), times 1/W rounded once."""
+    inv = np.float32(1.0 / float(w))
+    x = (k.astype(np.float32) + np.float32(0.5)).astype(np.float64)
+    assert np.all(x == k.astype(np.float64) + 0.5)
+    return (x * np.float64(inv)).astype(np.float32).astype(np.int64)  # the product fits in 53 bits
+
+
 @pytest.fixture(scope="module")
 def keys():
     return np.arange(LIMIT, dtype=np.int64)
@@ -34,6 +45,7 @@ def test_fast_decode_is_exact_below_2_pow_22(keys, w):
     q = fast_quotient(keys, w)
     bad = np.nonzero(q != keys // w)[0]
     assert bad.size == 0, f"W={w}: first wrong k={bad[:5]}"
+    assert np.array_equal(kernel_quotient(keys, w), q)
 
 
 def test_the_bound_is_needed():

@@ -94,8 +94,11 @@ struct WindowParams {
   float invtxn, invtyn, invpxn, invpyn;
 };
 
-// (int)fma(k, inv, inv / 2) = k / n for 0 <= k < 2^22 and inv = 1/n in fp32.
-__device__ __forceinline__ int div_small(int k, float inv) { return (int)__builtin_fmaf((float)k, inv, 0.5f * inv); }
+// (int)fma(k, inv, inv / 2) = k / n for 0 <= k < 2^22 and inv = 1/n in fp32,
+// written as (int)((k + 0.5) * inv): k + 0.5 is exact in fp32 and the product
+// rounds the same exact value once, so the bits agree, and a uniform inv
+// stays a scalar operand (a vector instruction takes at most one).
+__device__ __forceinline__ int div_small(int k, float inv) { return (int)(((float)k + 0.5f) * inv); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -358,8 +361,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // row wrap, [wlo, wend) counted from the run's start as W - c0 + column.
   // The patch layout tests rows and columns on their own: the query sees
   // grid rows [ylo, yend) and columns [clo, cend).
-  int flo[2] = {0, 0}, ylo[2] = {0, 0}, clo[2] = {0, 0}, cend[2] = {0, 0};
-  int wlo[2] = {0, 0}, wend[2] = {0, 0}, yend[2] = {0, 0};
+  int flo[2] = {0, 0}, ylo[2] = {0, 0}, clo[2] = {0, 0}, cend[2] = {0, 0}, yend[2] = {0, 0};
+  // (wlo and wend follow from clo and cend; formed where used)
+  auto wlo = [&](int h) __attribute__((always_inline)) { return wp.W + (clo[h] > 0 ? clo[h] : 0); };
+  auto wend = [&](int h) __attribute__((always_inline)) { return wp.W + cend[h]; };
   if constexpr (WIN != kWinNone) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -380,8 +385,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       clo[h] = qx - wp.rw;
       const int chi = qx + wp.rw < wp.W - 1 ? qx + wp.rw : wp.W - 1;
       cend[h] = chi + 1;
-      wlo[h] = wp.W + (clo[h] > 0 ? clo[h] : 0);
-      wend[h] = wp.W + chi + 1;
       yend[h] = (qy + wp.rh < wp.H - 1 ? qy + wp.rh : wp.H - 1) + 1;
     }
   }
@@ -512,7 +515,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     if constexpr (WIN == kWinRows) {
       const int base = tile * KT;
       const unsigned fspan = 2u * wp.rf, yspan = 2u * wp.rh, xspan = 2u * wp.rw;
-      const float hinvW = 0.5f * wp.invW, hinvH = 0.5f * wp.invH;
       if (wp.mode == 2) {
         // the tile [base, base + 64) lies in rows rb and rb + 1; the visible
         // keys of each row form one range of tile offsets
@@ -521,9 +523,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           const int hi = b < lo ? lo : (b > 64 ? 64 : b);
           return hi == lo ? (uint64_t)0 : ((~(uint64_t)0 >> (64 - hi)) & (~(uint64_t)0 << lo));
         };
-        const int rb = (int)__builtin_fmaf((float)base, wp.invW, hinvW);
+        const int rb = div_small(base, wp.invW);
         const int cb = base - __mul24(rb, wp.W);
-        const int fb = (int)__builtin_fmaf((float)rb, wp.invH, hinvH);
+        const int fb = div_small(rb, wp.invH);
         const int yb = rb - __mul24(fb, wp.H);
         const bool wrap = yb == wp.H - 1;
         const int y1 = wrap ? 0 : yb + 1;
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
           const bool row0 = ((unsigned)(fb - flo[h]) <= fspan) & ((unsigned)(yb - ylo[h]) <= yspan);
           const bool row1 = ((unsigned)(f1 - flo[h]) <= fspan) & ((unsigned)(y1 - ylo[h]) <= yspan);
           const uint64_t mm = (row0 ? bits64(clo[h] - cb, cend[h] - cb) : (uint64_t)0) |
-                              (row1 ? bits64(wlo[h] - cb, wend[h] - cb) : (uint64_t)0);
+                              (row1 ? bits64(wlo(h) - cb, wend(h) - cb) : (uint64_t)0);
           // this lane's keys are the runs at tile offsets 8r and 32 + 8r:
           // bytes r and 4 + r of mm
           const unsigned lo = (unsigned)mm, hi = (unsigned)(mm >> 32);
@@ -551,9 +553,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
 #pragma unroll
         for (int s = 0; s < MS; ++s) {
           const int k0 = base + 32 * s + 8 * r4;
-          const int r0 = (int)__builtin_fmaf((float)k0, wp.invW, hinvW);
+          const int r0 = div_small(k0, wp.invW);
           const int c0 = k0 - __mul24(r0, wp.W);
-          const int f0 = (int)__builtin_fmaf((float)r0, wp.invH, hinvH);
+          const int f0 = div_small(r0, wp.invH);
           const int y0 = r0 - __mul24(f0, wp.H);
           const bool wrap = y0 == wp.H - 1;
           const int y1 = wrap ? 0 : y0 + 1;
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
             const bool row0 = ((unsigned)(f0 - flo[h]) <= fspan) & ((unsigned)(y0 - ylo[h]) <= yspan);
             const bool row1 = ((unsigned)(f1 - flo[h]) <= fspan) & ((unsigned)(y1 - ylo[h]) <= yspan);
             const unsigned rv =
-                (row0 ? bits(clo[h] - c0, cend[h] - c0) : 0u) | (row1 ? bits(wlo[h] - c0, wend[h] - c0) : 0u);
+                (row0 ? bits(clo[h] - c0, cend[h] - c0) : 0u) | (row1 ? bits(wlo(h) - c0, wend(h) - c0) : 0u);
             vis |= rv << (16 * h + 8 * s);
           }
         }
@@ -721,15 +723,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     constexpr int NB = NOP / RB;
     // scheduling groups that keep the batch structure of batches b0 .. b1:
     // the reads of batch b + 1, then the MFMAs of batch b (two per operand)
-    // (the patch layout's box MFMAs join the batch of the first K operand)
     constexpr bool kBox = WIN == kWinPatch && decltype(SC)::value;
     auto groups = [&](int b0, int b1) __attribute__((always_inline)) {
       for (int b = b0; b <= b1; ++b) {
         if (b + 1 < NB) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
-        if (kBox && b == NV / RB)
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB + 2 * NKB, 0);  // MFMA
-        else
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);  // MFMA
       }
     };
     // Operand i < NV is V block i = (s, db) (db fastest, workspace order),
@@ -740,25 +738,37 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
     auto addr = [&](int i) __attribute__((always_inline)) {
       return st + (i < NV ? TILE + i * 1024 : kbs(i - NV) * 1024);
     };
-    // accumulator input of the first score MFMA per key block and half: -m,
-    // or -inf for a key outside the window (sign-extended bit, then a bit
-    // select)
-    f32x4 cneg[NKB][2];
+    // accumulator input of the first score MFMA of key block kb and half h:
+    // -m, or -inf for a key outside the window (sign-extended bit, then a bit
+    // select), formed right before that MFMA so that only the window bits
+    // stay live through the P.V products
     if constexpr (kBox) wvis = vis_sc;
-    if constexpr (WIN == kWinRows && decltype(SC)::value) {
-      const unsigned vis = window_vis(tw[1]);
-      wvis = vis;
+    if constexpr (WIN == kWinRows && decltype(SC)::value) wvis = window_vis(tw[1]);
+    auto cneg = [&](int kb, int h) __attribute__((always_inline)) {
+      f32x4 c;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int i = 0; i < 4; ++i) {
+        const unsigned keep = (unsigned)((int)(wvis << (31 - (16 * h + 4 * kb + i))) >> 31);
+        const float mv = negm[h][i];  // (bit-casting the element expression itself reads element 0)
+        const unsigned mb = __builtin_bit_cast(unsigned, mv);
+        c[i] = __builtin_bit_cast(float, (mb & keep) | (0xff800000u & ~keep));
+      }
+      return c;
+    };
+    // Patch layout: the box products come first, fenced off, so that the
+    // P.V products stand between them and the score products that take their
+    // results (a phase without P.V products waits instead); see the note on
+    // matrix-core hand-offs above.
+    if constexpr (kBox) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k2 = 0; k2 < NKB; ++k2)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const unsigned keep = (unsigned)((int)(vis << (31 - (16 * h + 4 * kb + i))) >> 31);
-            const float mv = negm[h][i];  // (bit-casting the element expression itself reads element 0)
-            const unsigned mb = __builtin_bit_cast(unsigned, mv);
-            cneg[kb][h][i] = __builtin_bit_cast(float, (mb & keep) | (0xff800000u & ~keep));
-          }
+          sacc[k2][h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(onehot[k2], pen_sc[h], negm[h], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NV == 0) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+      __builtin_amdgcn_sched_barrier(0);
     }
     u32x4 buf[2][RB];
 #pragma unroll
@@ -781,20 +791,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pk[s][h], oacc[db][h], 0, 0, 0);
         } else {
           const int kb = (i - NV) % NKB, s = (i - NV) / NKB;
-          if constexpr (kBox) {
-            if (i == NV) {
-#pragma unroll
-              for (int k2 = 0; k2 < NKB; ++k2)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                  sacc[k2][h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(onehot[k2], pen_sc[h], negm[h], 0, 0, 0);
-            }
-          }
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const f32x4 c0 = WIN == kWinPatch ? sacc[kb][h] : (WIN == kWinRows ? cneg[kb][h] : negm[h]);
-            sacc[kb][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), qreg[s][h],
-                                                                 s == 0 ? c0 : sacc[kb][h], 0, 0, 0);
+            f32x4 c0 = s == 0 ? negm[h] : sacc[kb][h];
+            if constexpr (WIN == kWinPatch) c0 = sacc[kb][h];
+            if constexpr (WIN == kWinRows)
+              if (s == 0) c0 = cneg(kb, h);
+            sacc[kb][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), qreg[s][h], c0, 0, 0, 0);
           }
         }
       }
@@ -858,9 +861,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   // (scores: the wave needs tile t; else its probabilities are set to 0,
   // which is what the softmax would give, so a P.V product that still runs
   // adds exact zeros)
-  auto sm = [&](auto FILL, int t, int fill_tile, int i, auto SUM, bool scores) __attribute__((always_inline)) {
+  auto sm = [&](bool fill, int t, int fill_tile, int i, auto SUM, bool scores) __attribute__((always_inline)) {
     if constexpr (SPARSE) __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(FILL)::value) issue(fill_tile, tile_k(NS, i), tile_k(NS - 1, i));
+    if (fill) issue(fill_tile, tile_k(NS, i), tile_k(NS - 1, i));
     prefetch(i);
     if (scores) {
       softmax(t, SUM);
@@ -891,32 +894,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
   auto need = [](bool b) __attribute__((always_inline)) { return WIN != kWinPatch || b; };
   bool pv = false;
   if (group == 0) {  // period i: GEMM_i then SOFTMAX_i (with the row sums)
-    if (NS - 1 <= nt) {
+    {
       const bool sc = prep_scores(tile_k(1, 0));
       if (need(sc)) gemm(F{}, T{}, 0, F{}, F{}, nob);
-      sm(T{}, tile_k(1, 0), NS - 1, 0, T{}, need(sc));
-      pv = sc;
-    } else {
-      const bool sc = prep_scores(tile_k(1, 0));
-      if (need(sc)) gemm(F{}, T{}, 0, F{}, F{}, nob);
-      sm(F{}, tile_k(1, 0), 0, 0, T{}, need(sc));
+      sm(NS - 1 <= nt, tile_k(1, 0), NS - 1, 0, T{}, need(sc));
       pv = sc;
     }
-    int j = 1;
-    for (; j < nt && j + NS - 1 <= nt; ++j) {
+    // one loop for the refill periods and the drain periods (a uniform
+    // branch skips the refill), so the accumulators keep one set of
+    // registers throughout
+    for (int j = 1; j < nt; ++j) {
       advance();
       tile_barrier(j);
       const bool sc = prep_scores(tile_k(1, j));
       if (need(pv || sc)) gemm(T{}, T{}, j, F{}, F{}, nob);
-      sm(T{}, tile_k(1, j), j + NS - 1, j, T{}, need(sc));
-      pv = sc;
-    }
-    for (; j < nt; ++j) {
-      advance();
-      tile_barrier(j);
-      const bool sc = prep_scores(tile_k(1, j));
-      if (need(pv || sc)) gemm(T{}, T{}, j, F{}, F{}, nob);
-      sm(F{}, tile_k(1, j), 0, j, T{}, need(sc));
+      sm(j + NS - 1 <= nt, tile_k(1, j), j + NS - 1, j, T{}, need(sc));
       pv = sc;
     }
     tile_barrier(nt);
@@ -943,13 +935,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
         const bool run = pv || sc;
         Batch pre{};
         if (run) pre = first_batch(jj);
-        sm(F{}, tile_k(0, jj), 0, jj, F{}, pv);
+        sm(false, tile_k(0, jj), 0, jj, F{}, pv);
         lists_landed();
         if (run) gemm(T{}, T{}, jj, T{}, T{}, pre);
         pv = sc;
       } else {
         const Batch pre = first_batch(jj);
-        sm(F{}, tile_k(0, jj), 0, jj, F{}, true);
+        sm(false, tile_k(0, jj), 0, jj, F{}, true);
         lists_landed();
         gemm(T{}, T{}, jj, T{}, T{}, pre);
       }
