@@ -192,7 +192,13 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
       *reinterpret_cast<half8*>(wt + (t + 256 * r) * 16) = h;
     }
 
-    // values: stage the row-major tile in LDS, then gather 8 keys per slot
+    // values: stage the row-major tile in LDS, then gather 8 keys per slot.
+    // The gather reads, per instruction, one head-dim column pair of 16 lanes
+    // in each of the row groups 8r + j (r < 4); row R keeps its 16-byte chunk
+    // c at chunk c ^ 2((R >> 3) & 3), so the four groups read four disjoint
+    // 32-byte windows of LDS banks (padding alone cannot separate rows 8
+    // apart while rows stay 16-byte aligned).
+    auto swz = [](int row) __attribute__((always_inline)) { return 2 * ((row >> 3) & 3); };
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < SLOTS; ++r) {
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
       u32x4 w = {0u, 0u, 0u, 0u};
       const int n = map.token<PATCH>(tile, row, N);
       if (n >= 0) w = *reinterpret_cast<const u32x4*>(Vbh + (int64_t)n * D + 8 * col8);
-      *reinterpret_cast<u32x4*>(vs + row * VPAD + 8 * col8) = w;
+      *reinterpret_cast<u32x4*>(vs + row * VPAD + 8 * (col8 ^ swz(row))) = w;
     }
     __syncthreads();
 #pragma unroll
@@ -211,11 +217,12 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const uint16_t* __restrict
       const int i = lane & 15, rr = lane >> 4;
       const int ks = blk / DB, db = blk - ks * DB;
       const int col = 16 * db + i;
-      const int key0 = 32 * ks + 8 * rr;
+      const int key0 = 32 * ks + 8 * rr;  // rows key0 .. key0 + 7 share swz = 2 rr
+      const int scol = 8 * ((col >> 3) ^ (2 * rr)) + (col & 7);
       u32x4 w;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        w[j] = (uint32_t)vs[(key0 + 2 * j) * VPAD + col] | ((uint32_t)vs[(key0 + 2 * j + 1) * VPAD + col] << 16);
+        w[j] = (uint32_t)vs[(key0 + 2 * j) * VPAD + scol] | ((uint32_t)vs[(key0 + 2 * j + 1) * VPAD + scol] << 16);
       *reinterpret_cast<u32x4*>(wt + TILE + slot * 16) = w;
     }
   }
