@@ -757,10 +757,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(
       }
       return c;
     };
-    // Patch layout: the box products come first, fenced off, so that the
-    // P.V products stand between them and the score products that take their
-    // results (a phase without P.V products waits instead); see the note on
-    // matrix-core hand-offs above.
+    // Patch layout: the box products run first, as a fenced group, so that
+    // the P.V products stand between them and the score products that take
+    // their results as accumulator input (a phase without P.V products waits
+    // 32 cycles instead). With a 16x16x16 box product and a 16x16x32 score
+    // product next to each other on one accumulator register (written, then
+    // read as accumulator input one instruction later, or read, then
+    // overwritten), the scores came out wrong on gfx950, and the compiler
+    // inserted no wait states there; tests/test_sources.py checks the
+    // generated code for such pairs.
     if constexpr (kBox) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
